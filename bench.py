@@ -1,0 +1,268 @@
+#!/usr/bin/env python3
+"""Benchmark of the grouped MXFP8 weight gradient (and the other passes).
+
+Default (the headline): E=8 experts, M=N=K=8192, per-expert token counts
+[3200, 1536, 1024, 640, 512, 512, 384, 384] (Zipf(1.1) in 128-token units),
+g^T and x^T ~ normal(0,1) with 1% of entries x64, MX-quantised on the GPU by
+moe_gg_mx_quantize before timing.  One step = one moe_gg_wgrad_mxfp8 call
+(expert bounds, operand staging, scale packing, block-scaled MFMA, bf16
+epilogue) over resident inputs.  Prints one JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--gpus 1]
+  python bench.py --pass dgrad --workload 5      # other passes / workloads
+  python bench.py --pass quantize --workload 4
+
+Timing: HIP events on the stream the kernels are launched on (torch's
+current stream), bracketing the K timed steps after a synchronize.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as wl  # noqa: E402
+
+# MI355X published dense peaks (per GPU)
+PEAK_FP8_TFLOPS = 5000.0
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+KERNEL_SOURCES = {
+    "wgrad": ["wgrad_mxfp8.hip", "common.hpp"],
+    "dgrad": ["dgrad_f32.hip", "common.hpp"],
+    "quantize": ["mx_quantize.hip", "common.hpp"],
+}
+KERNEL_NAMES = {"wgrad": "wgrad_mxfp8_kernel", "dgrad": "dgrad_f32_kernel", "quantize": "mx_quantize_kernel"}
+
+
+def source_digest(pass_name: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[pass_name]:
+        with open(os.path.join(ROOT, "moe_grouped_gemm_mxfp8_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(pass_name: str, workload: int):
+    """HBM bytes per launch from the committed counter summary, if it matches the current kernel."""
+    path = os.path.join(ROOT, "profiles", f"{pass_name}_w{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_digest") != source_digest(pass_name):
+        return None
+    try:
+        return int(float(vals["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_info():
+    model = platform.processor() or "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            return int(info[0]["num_threads"])
+    except Exception:
+        pass
+    return os.cpu_count() or 1
+
+
+def time_steps(torch, fn, steps, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps  # ms per step
+
+
+def bench_wgrad(torch, mg, idx, steps, warmup, cpu_baseline, fast=False):
+    w = wl.WORKLOADS[idx]
+    inp = wl.make_wgrad_inputs(idx)
+    d = torch.device("cuda:0")
+    off_np = inp["off"]
+    gT = torch.from_numpy(inp["gT"]).to(d)
+    xT = torch.from_numpy(inp["xT"]).to(d)
+    qa, sa = mg.mx_quantize(gT)
+    qb, sb = mg.mx_quantize(xT)
+    off = torch.from_numpy(off_np).to(d)
+    del gT, xT
+    out = torch.empty((w.E * w.N, w.K), dtype=torch.bfloat16, device=d)
+    torch.cuda.synchronize()
+    ms = time_steps(torch, lambda: mg.wgrad_mxfp8(qa, qb, sa, sb, off, out=out, fast=fast), steps, warmup)
+    tokens = int(off_np[-1] - off_np[0])
+    flop = 2.0 * w.N * w.K * tokens
+    algo_bytes = (w.N + w.K) * w.M + (w.N + w.K) * (w.M // 32) + 2 * w.E * w.N * w.K
+    tflops = flop / (ms * 1e-3) / 1e12
+    line = {
+        "metric": "TFLOP/s + % of fp8 MFMA peak, MXFP8 wgrad M=N=K=8192 E=8 (1 GPU)" if idx == 4
+        else f"TFLOP/s, MXFP8 grouped wgrad workload {idx}",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "pct_of_fp8_peak": round(100.0 * tflops / PEAK_FP8_TFLOPS, 2),
+        "ms_per_step": round(ms, 4),
+        "dtype": "fp8e4m3*fp8e4m3->f32 acc, bf16 out",
+        "mode": "single block-scaled MFMA pass (hardware run-of-8 rounding)" if fast
+        else "two block-scaled MFMA passes (g^T codes >= 128 / the rest); within the exact-sum tolerance",
+        "config": {"workload": w.name, "E": w.E, "M": w.M, "N": w.N, "K": w.K,
+                   "tokens_per_expert": [int(c) for c in np.diff(off_np)]},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP8_TFLOPS, 4),
+                     "traffic": read_traffic("wgrad", idx),
+                     "algorithmic_bytes": algo_bytes, "algorithmic_flop": flop,
+                     "hbm_gbs_algorithmic": round(algo_bytes / (ms * 1e-3) / 1e9, 1)},
+    }
+    if cpu_baseline:
+        line["cpu_baseline"] = cpu_wgrad_baseline(inp)
+    return line
+
+
+def cpu_wgrad_baseline(inp):
+    """The oracle (numpy fp64) on the whole workload, timed on this host."""
+    import oracle
+    gT, xT, off = inp["gT"], inp["xT"], inp["off"]
+    ca, sa = oracle.mx_quantize(gT)          # input preparation, not timed
+    cb, sb = oracle.mx_quantize(xT)
+    t0 = time.perf_counter()
+    ref = oracle.wgrad(ca, sa, cb, sb, off)   # dequantise + per-expert fp64 GEMM
+    dt = time.perf_counter() - t0
+    del ref
+    tokens = int(off[-1] - off[0])
+    flop = 2.0 * gT.shape[0] * xT.shape[0] * tokens
+    return {"value": round(flop / dt / 1e12, 4), "unit": "TFLOP/s", "cores": blas_threads(),
+            "kind": "oracle", "seconds": round(dt, 2), "cpu": cpu_info(),
+            "sample": "the whole workload: MX dequantise to fp64 + one fp64 matmul per expert "
+                      "(oracle.wgrad); quantisation of the inputs not timed"}
+
+
+def bench_dgrad(torch, mg, idx, steps, warmup, cpu_baseline):
+    w = wl.WORKLOADS[idx]
+    inp = wl.make_dgrad_inputs(idx)
+    d = torch.device("cuda:0")
+    g = torch.from_numpy(inp["g"]).to(d)
+    W = torch.from_numpy(inp["W"]).to(d)
+    off = torch.from_numpy(inp["off"]).to(d)
+    out = torch.empty((w.M, w.K), dtype=torch.float32, device=d)
+    ms = time_steps(torch, lambda: mg.dgrad_f32(g, W, off, out=out), steps, warmup)
+    flop = 2.0 * w.M * w.N * w.K
+    nonempty = int(np.count_nonzero(np.diff(inp["off"])))
+    algo_bytes = 4 * (w.M * w.N + nonempty * w.N * w.K + w.M * w.K)
+    tflops = flop / (ms * 1e-3) / 1e12
+    line = {
+        "metric": f"TFLOP/s, f32 grouped dgrad workload {idx}",
+        "value": round(tflops, 2), "unit": "TFLOP/s",
+        "pct_of_f32_peak": round(100 * tflops / PEAK_F32_TFLOPS, 2),
+        "ms_per_step": round(ms, 4), "dtype": "f32",
+        "config": {"workload": w.name, "E": w.E, "M": w.M, "N": w.N, "K": w.K},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_F32_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_F32_TFLOPS, 4),
+                     "traffic": read_traffic("dgrad", idx), "algorithmic_bytes": algo_bytes},
+    }
+    if cpu_baseline:
+        import oracle
+        t0 = time.perf_counter()
+        oracle.dgrad(inp["g"], inp["W"], inp["off"])
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": round(flop / dt / 1e12, 4), "unit": "TFLOP/s", "cores": blas_threads(),
+                                "kind": "oracle", "seconds": round(dt, 2), "cpu": cpu_info(),
+                                "sample": "the whole workload (oracle.dgrad, fp64)"}
+    return line
+
+
+def bench_quantize(torch, mg, idx, steps, warmup, cpu_baseline):
+    inp = wl.make_wgrad_inputs(idx)
+    d = torch.device("cuda:0")
+    x = torch.from_numpy(inp["xT"]).to(d)
+    R, L = x.shape
+    q = torch.empty((R, L), dtype=torch.uint8, device=d)
+    s = torch.empty((R, L // 32), dtype=torch.uint8, device=d)
+    ms = time_steps(torch, lambda: mg.mx_quantize(x, q, s), steps, warmup)
+    nbytes = 4 * R * L + R * L + R * L // 32
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    line = {"metric": f"GB/s, MX quantise of x^T, workload {idx}", "value": round(gbs, 1), "unit": "GB/s",
+            "ms_per_step": round(ms, 4), "dtype": "f32->e4m3+e8m0",
+            "config": {"workload": wl.WORKLOADS[idx].name, "R": R, "L": L},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": read_traffic("quantize", idx)}}
+    if cpu_baseline:
+        import oracle
+        sub = inp["xT"][: max(1, R // 8)]
+        t0 = time.perf_counter()
+        oracle.mx_quantize(sub)
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": round(5.03125 * sub.size / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+                                "kind": "oracle", "seconds": round(dt, 2), "cpu": cpu_info(),
+                                "sample": f"rows 0..{sub.shape[0]} of x^T (oracle.mx_quantize)"}
+    return line
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--pass", dest="pass_name", choices=["wgrad", "dgrad", "quantize"], default="wgrad")
+    ap.add_argument("--workload", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fast", action="store_true", help="wgrad: the single-pass entry point")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the kernels run on a single MI355X and this build "
+              "has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import moe_grouped_gemm_mxfp8_amd as mg
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    idx = args.workload or {"wgrad": 4, "dgrad": 5, "quantize": 4}[args.pass_name]
+    fn = {"wgrad": bench_wgrad, "dgrad": bench_dgrad, "quantize": bench_quantize}[args.pass_name]
+    kw = {"fast": True} if (args.fast and args.pass_name == "wgrad") else {}
+    line = fn(torch, mg, idx, args.steps, args.warmup, not args.no_cpu_baseline, **kw)
+    line.update({"n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                 "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+                 "data": "synthetic (seeded numpy generators, workload recipe)",
+                 "kernel": KERNEL_NAMES[args.pass_name], "kernel_source_digest": source_digest(args.pass_name)})
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,161 @@
+/*
+ * moe_gg.h -- C ABI of the MI355X (gfx950) MoE grouped-GEMM backward library.
+ *
+ * The library computes the two backward GEMMs of a mixture-of-experts layer
+ * whose token rows are bucketed by expert through an offset array:
+ *
+ *   weight gradient  grad_w[e] = g[o_e:o_{e+1}]^T . x[o_e:o_{e+1}]
+ *                    (MXFP8 inputs, f32 accumulation, bf16 output)
+ *   data gradient    dx[r]     = g[r] . W_{e(r)}        (f32)
+ *
+ * plus the MX quantiser that produces the weight gradient's inputs.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers (hipMalloc'd or equivalent),
+ *     row-major, densely packed, with the layouts stated below.
+ *   - Calls enqueue work on `stream` (0 = the null stream) and return without
+ *     synchronising.  Errors found on the host come back as a negative
+ *     status before anything is enqueued; a device fault shows at the
+ *     caller's next synchronisation.
+ *   - The caller owns every buffer.  The library allocates no memory and
+ *     keeps no mutable global state: calls are reentrant and thread-safe.
+ *     Outputs are fully overwritten (no accumulate mode).
+ *   - The host never reads `expert_off` (device memory).  Offsets must satisfy
+ *     off[0] = 0, off[e] <= off[e+1], off[E] = M; a malformed array yields
+ *     unspecified values but no access outside the buffers (each bound is
+ *     clamped to [0, M], a decreasing pair counts as empty).
+ */
+#ifndef MOE_GG_H
+#define MOE_GG_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_GG_API __attribute__((visibility("default")))
+
+enum {
+  MOE_GG_OK = 0,
+  MOE_GG_EINVAL = -1,       /* null pointer, non-positive size, misaligned size   */
+  MOE_GG_EUNSUPPORTED = -2, /* valid request outside what the kernels tile        */
+  MOE_GG_ELAUNCH = -3       /* the HIP runtime refused the launch                 */
+};
+
+/*
+ * Grouped MXFP8 weight gradient.
+ *
+ * Source: the tinygrad page "grouped_mxfp8_wgrad.cpp" (kernel signature and
+ * its global layouts A = g^T, B = x^T, C = grad_w with the experts stacked;
+ * its k-loop over the expert's 128-token blocks; its epilogue, which stores
+ * the zero-initialised accumulators of an empty expert as they are).
+ *
+ *   A        g^T, E4M3 bytes [N][M]   (token axis contiguous)
+ *   B        x^T, E4M3 bytes [K][M]
+ *   C        grad_w, bf16 bits [E*N][K]; rows e*N..e*N+N-1 hold expert e;
+ *            every element is written, an empty expert's rows with +0.0
+ *   scale_A  E8M0 bytes [N][M/32]: scale of A[n][32j..32j+31] is 2^(s-127)
+ *   scale_B  E8M0 bytes [K][M/32]
+ *   expert_off int32 [E+1]; each offset a multiple of 128
+ *
+ *   grad_w[e*N+n][k] = bf16_rne( sum over m in [off[e], off[e+1]) of
+ *                        e4m3(A[n][m]) 2^(sA[n][m/32]-127) e4m3(B[k][m]) 2^(sB[k][m/32]-127) )
+ *   accumulated in f32.
+ *
+ * Shapes: M, N, K, E >= 1; M % 128 == 0 (EINVAL otherwise);
+ * N % 256 == 0 and K % 256 == 0 and E <= 1024 (EUNSUPPORTED otherwise).
+ * Offsets that are not multiples of 128 are unsupported: the kernel then
+ * truncates each expert's token count down to a multiple of 128.
+ *
+ * Accuracy: gfx950's block-scaled fp8 MFMA sums each run of 8 consecutive
+ * tokens after truncating every product toward zero to a multiple of
+ * 2^(floor(log2 p_max) - 13), p_max the largest product magnitude of the run
+ * (measured on the hardware; runs are then added exactly, the accumulator in
+ * f32).  A run whose products span more than 2^6 loses low bits.  This entry
+ * point therefore multiplies in two passes, the g^T codes of magnitude >= 128
+ * and the rest, so that no run mixes a block's largest codes with its small
+ * ones; the result stays within 2^-7 |ref| + 2^-12 rms(ref) of the exact sum
+ * also for blocks with 64x outliers.  Twice the MFMA work of one pass.
+ */
+MOE_GG_API int moe_gg_wgrad_mxfp8(const uint8_t *A, const uint8_t *B, uint16_t *C,
+                                  const uint8_t *scale_A, const uint8_t *scale_B,
+                                  const int32_t *expert_off, int M, int N, int K, int E,
+                                  hipStream_t stream);
+
+/*
+ * The same grouped MXFP8 weight gradient in ONE block-scaled MFMA pass: the
+ * hardware's own reduction as described above, half the MFMA work.  Same
+ * arguments, layouts, shapes and status codes as moe_gg_wgrad_mxfp8.  The
+ * result equals the exact sum when every 8-token run's products are within
+ * 2^6 of each other, and otherwise can differ by up to 2^-13 of the run's
+ * largest product per product.  For callers whose inputs have a moderate
+ * in-block range (no outliers) or who accept the hardware's rounding.
+ */
+MOE_GG_API int moe_gg_wgrad_mxfp8_fast(const uint8_t *A, const uint8_t *B, uint16_t *C,
+                                       const uint8_t *scale_A, const uint8_t *scale_B,
+                                       const int32_t *expert_off, int M, int N, int K, int E,
+                                       hipStream_t stream);
+
+/*
+ * Grouped f32 data gradient.
+ *
+ * Source: the oarust page "grouped_gemm_m_data_backward.slang" (push
+ * constants output_gradient, weight, offsets, input_gradient, rows,
+ * output_features, input_features, experts; the row -> expert scan
+ * expert_for_row; the per-row-expert dot products of tiles that span
+ * several experts; the overwriting store).
+ *
+ *   A   g  (output gradient), f32 [M][N]          N = output_features
+ *   B   W  (expert weights),  f32 [E][N][K]        K = input_features
+ *   C   dx (input gradient),  f32 [M][K]
+ *   expert_off int32 [E+1]; any nondecreasing values (no alignment needed)
+ *
+ *   dx[r][k] = sum_n g[r][n] W[e(r)][n][k],  e(r) the e with off[e] <= r < off[e+1],
+ *   f32 products and f32 accumulation.
+ *
+ * Shapes: M, N, K, E >= 1 (EINVAL otherwise); K % 4 == 0 and N % 4 == 0
+ * (EUNSUPPORTED otherwise).
+ */
+MOE_GG_API int moe_gg_dgrad_f32(const float *A, const float *B, float *C,
+                                const int32_t *expert_off, int M, int N, int K, int E,
+                                hipStream_t stream);
+
+/*
+ * MX quantiser: f32 [R][L] -> E4M3 codes [R][L] + E8M0 scales [R][L/32],
+ * blocks of 32 consecutive elements along L (aligned to the start of a row).
+ *
+ * Source: the 8192^3 workload's scale rule scale = 2^(floor(log2(blockmax)) - 8)
+ * and the decode page's mx8_scale / mx8_q (scale byte clamped to [1, 254];
+ * elements clamped to +-448 before the conversion).
+ *
+ *   s = clamp(floor(log2(max |X[r][32j..32j+31]|)) - 8 + 127, 1, 254), s = 1 for a zero block
+ *   Q[r][i] = e4m3_rne_saturate(X[r][i] * 2^(127 - s)); the sign of zero is kept
+ *
+ * Inputs must be finite (NaN/Inf give unspecified codes).
+ * Shapes: R >= 1, L >= 32, L % 32 == 0 (EINVAL otherwise).
+ */
+MOE_GG_API int moe_gg_mx_quantize(const float *X, uint8_t *Q, uint8_t *S, int R, int L,
+                                  hipStream_t stream);
+
+/*
+ * Row -> expert map, the integer step of the data gradient, exposed so that
+ * it can be checked exactly: out[r] = the e with off[e] <= r < off[e+1] for r
+ * in [0, M), computed by the same device function the data-gradient kernel
+ * uses (source: the oarust page's expert_for_row).
+ *
+ *   expert_off int32 [E+1] (device), out int32 [M] (device).
+ * Shapes: M, E >= 1 (EINVAL otherwise).
+ */
+MOE_GG_API int moe_gg_row_experts(const int32_t *expert_off, int E, int M, int32_t *out,
+                                  hipStream_t stream);
+
+/* Static, never-NULL description of a status code. */
+MOE_GG_API const char *moe_gg_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_GG_H */

@@ -1,0 +1,21 @@
+"""MI355X (gfx950) MoE grouped-GEMM backward: MXFP8 weight gradient and f32
+data gradient, as hand-written HIP kernels behind a C ABI (include/moe_gg.h).
+
+Python entry points (thin wrappers over the C ABI; torch supplies device
+memory and the current stream, nothing else):
+
+  wgrad_mxfp8(a, b, scale_a, scale_b, expert_off, out=None, fast=False) -> bf16 [E*N, K]
+  dgrad_f32(g, w, expert_off, out=None)                     -> f32 [M, K]
+  mx_quantize(x, q=None, s=None)                            -> (uint8 [R, L], uint8 [R, L/32])
+  row_experts(expert_off, M, out=None)                      -> int32 [M]
+
+There is no CPU fallback: calling any of them without the built library or
+without a GPU raises.
+"""
+from __future__ import annotations
+
+from ._lib import EINVAL, ELAUNCH, EUNSUPPORTED, OK, MoeGGError, status_string
+from .ops import dgrad_f32, mx_quantize, row_experts, wgrad_mxfp8
+
+__all__ = ["wgrad_mxfp8", "dgrad_f32", "mx_quantize", "row_experts", "status_string",
+           "MoeGGError", "OK", "EINVAL", "EUNSUPPORTED", "ELAUNCH"]

@@ -1,0 +1,363 @@
+// Grouped MXFP8 weight gradient on gfx950:
+//   grad_w[e*N + n][k] = sum over tokens m of expert e of  g^T[n][m] x^T[k][m]
+// with E4M3 elements and one E8M0 scale per 32 tokens, f32 accumulation in
+// the block-scaled MFMA, bf16 output (the tinygrad page "grouped_mxfp8_wgrad.cpp":
+// its global layouts, the per-expert 128-token k-loop and the epilogue).
+//
+// Design (gfx950):
+//  * Persistent grid, one 512-thread workgroup per CU.  Output tiles are
+//    256 (k) x 256 (n) of one expert; every expert owns (K/256)(N/256) tiles.
+//    Tiles are ordered expert by expert, the experts with the most 128-token
+//    steps first (ranked once per workgroup from the offsets), and dealt
+//    round-robin to the workgroups, so the long tiles start first.  Inside an
+//    expert the tile order keeps the tiles that run at the same time on one
+//    XCD (blockIdx mod 8) in one 4 x 8 patch, so they share operand rows in
+//    that XCD's L2.
+//  * Each 128-token step stages x^T[256 x 128] and g^T[256 x 128] fp8 (32 KB
+//    each) plus their 256 scale dwords in LDS, with buffer loads that write
+//    LDS directly (no VGPR round trip), double-buffered: step s+1 is in
+//    flight while step s is multiplied.  The 16-byte chunks of each 128-byte
+//    LDS row are XOR-swizzled by (row/2) mod 8 so that the MFMA operand reads
+//    (16 rows x 16 bytes per pass) hit distinct banks.
+//  * 8 waves as 2 (k) x 4 (n); each wave owns a 128 x 64 output patch as
+//    4 x 2 accumulators of v_mfma_scale_f32_32x32x64_f8f6f4.  x^T is the
+//    MFMA A operand (rows = k) and g^T the B operand (columns = n), so each
+//    lane ends with 4 consecutive k of one output row n, stored as 8 bytes.
+//  * Operand lane layout of the scaled MFMA (measured on gfx950, the decode
+//    page's lds_b8 note says the same for 16x16x128): lane l holds row l%32;
+//    lane group g = l/32 holds tokens 16g..16g+15 and 32+16g..32+16g+15 of the
+//    64-token half; the scale of lane l covers row l%32, 32-token block g of
+//    the half.  The four scale bytes of a row for one 128-token step are one
+//    dword (scales are row-major [rows][M/32]); shifted right by 8g it serves
+//    both halves through op_sel = 0 and 2.
+#include "common.hpp"
+#include "../../include/moe_gg.h"
+
+namespace moe_gg {
+namespace {
+
+constexpr int TK = 256;             // output k per tile  (rows of x^T)
+constexpr int TN = 256;             // output n per tile  (rows of g^T)
+constexpr int TT = 128;             // tokens per pipeline step
+constexpr int NWAVE = 8;
+constexpr int NTHREAD = NWAVE * 64;
+constexpr int MAX_EXPERTS = 1024;
+
+constexpr int ST_X = 0;                       // x^T tile [256][128] fp8
+constexpr int ST_G = ST_X + TK * TT;          // g^T tile [256][128] fp8
+constexpr int ST_SX = ST_G + TN * TT;         // x^T scale dwords [256]
+constexpr int ST_SG = ST_SX + TK * 4;         // g^T scale dwords [256]
+constexpr int STAGE_BYTES = ST_SG + TN * 4;   // 67584
+constexpr int DMA_PER_STAGE = 9;              // per wave: 4 + 4 tile chunks, 1 scale chunk
+
+struct Tile {
+  int valid, e, nk, tok0, nt, kt;
+};
+
+__device__ __forceinline__ Tile tile_info(int t, int total, int T, int tilesK, const int *s_order,
+                                          const int32_t *__restrict__ off, int M) {
+  Tile ti;
+  ti.valid = t < total;
+  if (!ti.valid) { ti.e = ti.nk = ti.tok0 = ti.nt = ti.kt = 0; return ti; }
+  const int rank = t / T;
+  int u = t - rank * T;
+  ti.e = __builtin_amdgcn_readfirstlane(s_order[rank]);
+  const int o0 = clampi(off[ti.e], 0, M);
+  const int o1 = clampi(off[ti.e + 1], o0, M);
+  ti.tok0 = o0;
+  ti.nk = (o1 - o0) / TT;
+  // XCD-aware order: with T a multiple of 8, the tiles a workgroup on XCD x
+  // gets (u = x mod 8) become a contiguous run of T/8 in the grouped order.
+  if ((T & 7) == 0) u = (u & 7) * (T >> 3) + (u >> 3);
+  const int tilesN = T / tilesK;
+  constexpr int GROUP = 4;            // n-tiles per group
+  const int per_group = GROUP * tilesK;
+  const int grp = u / per_group;
+  const int first_n = grp * GROUP;
+  const int gsz = min(tilesN - first_n, GROUP);
+  const int w = u - grp * per_group;
+  ti.nt = first_n + w % gsz;
+  ti.kt = w / gsz;
+  return ti;
+}
+
+// Byte mask of the E4M3 codes in a dword whose magnitude is >= 128
+// (exponent field >= 14): 0xFF in those bytes, 0x00 elsewhere.
+__device__ __forceinline__ uint32_t big_code_mask(uint32_t x) {
+  const uint32_t m = ((x & 0x70707070u) + 0x10101010u) & 0x80808080u;
+  return (m << 1) - (m >> 7);
+}
+
+template <bool SPLIT>
+__global__ __launch_bounds__(NTHREAD, 1) void wgrad_mxfp8_kernel(
+    const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, uint16_t *__restrict__ C,
+    const uint8_t *__restrict__ SA, const uint8_t *__restrict__ SB,
+    const int32_t *__restrict__ off, int M, int N, int K, int E) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE_BYTES];
+  __shared__ int s_order[MAX_EXPERTS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tilesN = N / TN, tilesK = K / TK;
+  const int T = tilesN * tilesK;
+  const int total = E * T;
+
+  // ---- expert ranking: most 128-token steps first, ties by index --------
+  {
+    int *s_cnt = reinterpret_cast<int *>(smem);
+    for (int e = tid; e < E; e += NTHREAD) {
+      const int o0 = clampi(off[e], 0, M);
+      const int o1 = clampi(off[e + 1], o0, M);
+      s_cnt[e] = (o1 - o0) / TT;
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += NTHREAD) {
+      const int c = s_cnt[e];
+      int rank = 0;
+      for (int j = 0; j < E; ++j) {
+        const int cj = s_cnt[j];
+        rank += (cj > c) | ((cj == c) & (j < e));
+      }
+      s_order[rank] = e;
+    }
+    __syncthreads();
+  }
+
+  // ---- per-lane constants -------------------------------------------------
+  const uint32_t smem_base = lds_addr(smem);
+  const uint32_t Mb = static_cast<uint32_t>(M);
+  const uint32_t scale_row = Mb / 32;      // bytes per scale row
+  // tile DMA: wave w fills 1 KB chunks 4w..4w+3 of each operand tile; chunk q
+  // holds tile rows 8q..8q+7, lane L -> row 8q + L/8, LDS slot L%8, which
+  // takes the row's global 16-byte chunk (L%8) ^ ((row/2) mod 8).
+  uint32_t voff_t[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 8 * (wave * 4 + i) + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    voff_t[i] = static_cast<uint32_t>(r) * Mb + static_cast<uint32_t>(c) * 16u;
+  }
+  // scale DMA: waves 0-3 load x^T scale rows, waves 4-7 g^T scale rows, 64 rows each
+  const int srow = (wave & 3) * 64 + lane;
+  const uint32_t voff_s = static_cast<uint32_t>(srow) * scale_row;
+
+  // MFMA operand addressing
+  const int wk = wave >> 2, wn = wave & 3;
+  const int g = lane >> 5, l32 = lane & 31;
+  const int swz = (l32 >> 1) & 7;
+  uint32_t xrow[4], grow[2];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) xrow[a] = ST_X + (wk * 128 + a * 32 + l32) * TT;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) grow[b] = ST_G + (wn * 64 + b * 32 + l32) * TT;
+  uint32_t chunk_off[2][2];   // [half][piece] -> swizzled 16-byte chunk offset
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    chunk_off[h][0] = (((4 * h + g) ^ swz) * 16);
+    chunk_off[h][1] = (((4 * h + 2 + g) ^ swz) * 16);
+  }
+
+  auto issue_stage = [&](const Tile &ti, int s, uint32_t buf) {
+    const uint32_t tok = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(ti.tok0 + s * TT));
+    const v4i srd_x = make_srd(B + static_cast<size_t>(ti.kt) * TK * M, TK * Mb);
+    const v4i srd_g = make_srd(A + static_cast<size_t>(ti.nt) * TN * M, TN * Mb);
+    const uint32_t base = smem_base + buf * STAGE_BYTES;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      dma_b128(srd_x, voff_t[i], tok, __builtin_amdgcn_readfirstlane(base + ST_X + (wave * 4 + i) * 1024));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      dma_b128(srd_g, voff_t[i], tok, __builtin_amdgcn_readfirstlane(base + ST_G + (wave * 4 + i) * 1024));
+    const bool xs = wave < 4;
+    const uint8_t *sbase = xs ? SB + static_cast<size_t>(ti.kt) * TK * scale_row
+                              : SA + static_cast<size_t>(ti.nt) * TN * scale_row;
+    const v4i srd_s = make_srd(sbase, 256u * scale_row);
+    const uint32_t sdst = base + (xs ? ST_SX : ST_SG) + (wave & 3) * 256;
+    dma_b32(srd_s, voff_s, tok / 32, __builtin_amdgcn_readfirstlane(sdst));
+  };
+
+  v16f acc[4][2];
+  int t = blockIdx.x;
+  Tile cur = tile_info(t, total, T, tilesK, s_order, off, M);
+  uint32_t buf = 0;
+  if (cur.valid && cur.nk > 0) issue_stage(cur, 0, buf);
+
+  while (cur.valid) {
+    const int tn = t + gridDim.x;
+    const Tile nxt = tile_info(tn, total, T, tilesK, s_order, off, M);
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
+
+#pragma unroll 1
+    for (int s = 0; s < cur.nk; ++s) {
+      if (s + 1 < cur.nk) {
+        issue_stage(cur, s + 1, buf ^ 1);
+        wait_vmcnt<DMA_PER_STAGE>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      barrier();
+      const uint8_t *st = smem + buf * STAGE_BYTES;
+      uint32_t sx[4], sg[2];
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        sx[a] = *reinterpret_cast<const uint32_t *>(st + ST_SX + 4 * (wk * 128 + a * 32 + l32)) >> (8 * g);
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        sg[b] = *reinterpret_cast<const uint32_t *>(st + ST_SG + 4 * (wn * 64 + b * 32 + l32)) >> (8 * g);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        v8i xa[4], gb[2];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const v4i lo = *reinterpret_cast<const v4i *>(st + xrow[a] + chunk_off[h][0]);
+          const v4i hi = *reinterpret_cast<const v4i *>(st + xrow[a] + chunk_off[h][1]);
+          xa[a] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const v4i lo = *reinterpret_cast<const v4i *>(st + grow[b] + chunk_off[h][0]);
+          const v4i hi = *reinterpret_cast<const v4i *>(st + grow[b] + chunk_off[h][1]);
+          gb[b] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          v8i gop = gb[b];
+          if (SPLIT) {
+            // pass 1: the g^T codes of magnitude >= 128; pass 2 (below): the rest
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+              gop[i] = static_cast<int>(static_cast<uint32_t>(gb[b][i]) & big_code_mask(static_cast<uint32_t>(gb[b][i])));
+          }
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            if (h == 0)
+              acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                  xa[a], gop, acc[a][b], 0, 0, 0, static_cast<int>(sx[a]), 0, static_cast<int>(sg[b]));
+            else
+              acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                  xa[a], gop, acc[a][b], 0, 0, 2, static_cast<int>(sx[a]), 2, static_cast<int>(sg[b]));
+          }
+          if (SPLIT) {
+            v8i glo;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) glo[i] = gb[b][i] ^ gop[i];
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+              if (h == 0)
+                acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    xa[a], glo, acc[a][b], 0, 0, 0, static_cast<int>(sx[a]), 0, static_cast<int>(sg[b]));
+              else
+                acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    xa[a], glo, acc[a][b], 0, 0, 2, static_cast<int>(sx[a]), 2, static_cast<int>(sg[b]));
+            }
+          }
+        }
+      }
+      barrier();
+      buf ^= 1;
+    }
+
+    // every wave is past its last read of both stage buffers: start the next tile's first step
+    if (nxt.valid && nxt.nk > 0) issue_stage(nxt, 0, buf);
+
+    const size_t crow0 = static_cast<size_t>(cur.e) * N + static_cast<size_t>(cur.nt) * TN;
+    const int ccol0 = cur.kt * TK;
+    if (cur.nk == 0) {
+      // empty expert: +0.0 everywhere, written as whole 512-byte row segments
+      const v4i z = {0, 0, 0, 0};
+#pragma unroll 4
+      for (int p = 0; p < TN / 16; ++p) {
+        const int row = p * 16 + (tid >> 5);
+        __builtin_nontemporal_store(z, reinterpret_cast<v4i *>(C + (crow0 + row) * K + ccol0 + (tid & 31) * 8));
+      }
+    } else {
+      // ---- epilogue through LDS: bf16 tile rows of 512 bytes, stored whole ----
+      // staging row r (of 128) holds output row crow0 + half*128 + r; its 16-byte
+      // chunks are XOR-swizzled by (r mod 32) so the 8-byte writes of 32 rows spread
+      uint8_t *stg = smem + (buf ^ 1) * STAGE_BYTES;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        if ((wn >> 1) == half) {
+#pragma unroll
+          for (int b = 0; b < 2; ++b) {
+            const int r = (wn & 1) * 64 + b * 32 + l32;
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const int c = (wk * 128 + a * 32 + 8 * q) >> 3;       // 16-byte chunk of the row
+                const uint32_t lo = pack_bf16x2(acc[a][b][4 * q + 0], acc[a][b][4 * q + 1]);
+                const uint32_t hi = pack_bf16x2(acc[a][b][4 * q + 2], acc[a][b][4 * q + 3]);
+                typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+                *reinterpret_cast<u2 *>(stg + r * 512 + ((c ^ (r & 31)) << 4) + 8 * g) = (u2){lo, hi};
+              }
+          }
+        }
+        barrier();
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+          const int r = p * 16 + (tid >> 5);
+          const int c = tid & 31;
+          const v4i v = *reinterpret_cast<const v4i *>(stg + r * 512 + ((c ^ (r & 31)) << 4));
+          __builtin_nontemporal_store(v, reinterpret_cast<v4i *>(C + (crow0 + half * 128 + r) * K + ccol0 + c * 8));
+        }
+        barrier();
+      }
+    }
+    t = tn;
+    cur = nxt;
+  }
+  wait_vmcnt<0>();
+}
+
+}  // namespace
+}  // namespace moe_gg
+
+namespace moe_gg {
+namespace {
+int launch_wgrad(bool split, const uint8_t *A, const uint8_t *B, uint16_t *C, const uint8_t *scale_A,
+                 const uint8_t *scale_B, const int32_t *expert_off, int M, int N, int K, int E,
+                 hipStream_t stream) {
+  if (!A || !B || !C || !scale_A || !scale_B || !expert_off) return MOE_GG_EINVAL;
+  if (M <= 0 || N <= 0 || K <= 0 || E <= 0) return MOE_GG_EINVAL;
+  if (M % TT) return MOE_GG_EINVAL;
+  if (N % TN || K % TK || E > MAX_EXPERTS) return MOE_GG_EUNSUPPORTED;
+  // the buffer descriptors address one 256-row operand panel with 32-bit offsets
+  if (static_cast<uint64_t>(TK) * static_cast<uint64_t>(M) > 0xFFFFFFFFull) return MOE_GG_EUNSUPPORTED;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_GG_ELAUNCH;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return MOE_GG_ELAUNCH;
+  const int64_t total = static_cast<int64_t>(E) * (N / TN) * (K / TK);
+  if (total > 0x7FFFFFFF) return MOE_GG_EUNSUPPORTED;
+  const int grid = static_cast<int>(total < cus ? total : cus);
+  if (split)
+    hipLaunchKernelGGL(wgrad_mxfp8_kernel<true>, dim3(grid), dim3(NTHREAD), 0, stream, A, B, C, scale_A,
+                       scale_B, expert_off, M, N, K, E);
+  else
+    hipLaunchKernelGGL(wgrad_mxfp8_kernel<false>, dim3(grid), dim3(NTHREAD), 0, stream, A, B, C, scale_A,
+                       scale_B, expert_off, M, N, K, E);
+  return hipGetLastError() == hipSuccess ? MOE_GG_OK : MOE_GG_ELAUNCH;
+}
+}  // namespace
+}  // namespace moe_gg
+
+extern "C" MOE_GG_API int moe_gg_wgrad_mxfp8(const uint8_t *A, const uint8_t *B, uint16_t *C,
+                                             const uint8_t *scale_A, const uint8_t *scale_B,
+                                             const int32_t *expert_off, int M, int N, int K, int E,
+                                             hipStream_t stream) {
+  return moe_gg::launch_wgrad(true, A, B, C, scale_A, scale_B, expert_off, M, N, K, E, stream);
+}
+
+extern "C" MOE_GG_API int moe_gg_wgrad_mxfp8_fast(const uint8_t *A, const uint8_t *B, uint16_t *C,
+                                                  const uint8_t *scale_A, const uint8_t *scale_B,
+                                                  const int32_t *expert_off, int M, int N, int K, int E,
+                                                  hipStream_t stream) {
+  return moe_gg::launch_wgrad(false, A, B, C, scale_A, scale_B, expert_off, M, N, K, E, stream);
+}

@@ -1,0 +1,100 @@
+"""torch-tensor wrappers of the C ABI (checks dtypes/devices, passes pointers)."""
+from __future__ import annotations
+
+import torch
+
+from ._lib import call
+
+__all__ = ["wgrad_mxfp8", "dgrad_f32", "mx_quantize", "row_experts"]
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtypes) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device (cuda/hip) tensor, got {t.device}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+_U8 = (torch.uint8, torch.float8_e4m3fn, torch.float8_e8m0fnu) if hasattr(torch, "float8_e8m0fnu") \
+    else (torch.uint8, torch.float8_e4m3fn)
+
+
+def wgrad_mxfp8(a, b, scale_a, scale_b, expert_off, out=None, fast=False):
+    """grad_w[E*N, K] (bf16) from g^T codes a[N, M], x^T codes b[K, M], E8M0 scales [.., M/32].
+
+    fast=False: two MFMA passes, within 2^-7|ref| + 2^-12 rms(ref) of the exact sum.
+    fast=True: one pass with the hardware's 8-token truncating reduction.
+    """
+    _dev(a, "a", _U8); _dev(b, "b", _U8)
+    _dev(scale_a, "scale_a", _U8); _dev(scale_b, "scale_b", _U8)
+    _dev(expert_off, "expert_off", (torch.int32,))
+    if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[1]:
+        raise ValueError("a must be [N, M] and b [K, M]")
+    N, M = a.shape
+    K = b.shape[0]
+    E = expert_off.numel() - 1
+    if scale_a.shape != (N, M // 32) or scale_b.shape != (K, M // 32):
+        raise ValueError("scales must be [N, M/32] and [K, M/32]")
+    if out is None:
+        out = torch.empty((E * N, K), dtype=torch.bfloat16, device=a.device)
+    _dev(out, "out", (torch.bfloat16,))
+    if out.shape != (E * N, K):
+        raise ValueError("out must be [E*N, K]")
+    call("moe_gg_wgrad_mxfp8_fast" if fast else "moe_gg_wgrad_mxfp8", a.data_ptr(), b.data_ptr(), out.data_ptr(), scale_a.data_ptr(),
+         scale_b.data_ptr(), expert_off.data_ptr(), M, N, K, E, _stream())
+    return out
+
+
+def dgrad_f32(g, w, expert_off, out=None):
+    """dx[M, K] (f32) = g[M, N] . W[e(r)] with W [E, N, K]."""
+    _dev(g, "g", (torch.float32,)); _dev(w, "w", (torch.float32,))
+    _dev(expert_off, "expert_off", (torch.int32,))
+    if g.dim() != 2 or w.dim() != 3 or w.shape[1] != g.shape[1]:
+        raise ValueError("g must be [M, N] and w [E, N, K]")
+    M, N = g.shape
+    E, _, K = w.shape
+    if expert_off.numel() != E + 1:
+        raise ValueError("expert_off must have E+1 entries")
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.float32, device=g.device)
+    _dev(out, "out", (torch.float32,))
+    if out.shape != (M, K):
+        raise ValueError("out must be [M, K]")
+    call("moe_gg_dgrad_f32", g.data_ptr(), w.data_ptr(), out.data_ptr(), expert_off.data_ptr(),
+         M, N, K, E, _stream())
+    return out
+
+
+def mx_quantize(x, q=None, s=None):
+    """MX-quantise f32 x[R, L] along L: (E4M3 codes uint8 [R, L], E8M0 scales uint8 [R, L/32])."""
+    _dev(x, "x", (torch.float32,))
+    if x.dim() != 2:
+        raise ValueError("x must be [R, L]")
+    R, L = x.shape
+    if q is None:
+        q = torch.empty((R, L), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty((R, max(L // 32, 1)), dtype=torch.uint8, device=x.device)
+    _dev(q, "q", _U8); _dev(s, "s", _U8)
+    call("moe_gg_mx_quantize", x.data_ptr(), q.data_ptr(), s.data_ptr(), R, L, _stream())
+    return q, s
+
+
+def row_experts(expert_off, M, out=None):
+    """int32 [M]: the expert of each token row (the data-gradient kernel's lookup)."""
+    _dev(expert_off, "expert_off", (torch.int32,))
+    E = expert_off.numel() - 1
+    if out is None:
+        out = torch.empty((M,), dtype=torch.int32, device=expert_off.device)
+    _dev(out, "out", (torch.int32,))
+    call("moe_gg_row_experts", expert_off.data_ptr(), E, int(M), out.data_ptr(), _stream())
+    return out

@@ -1,0 +1,89 @@
+"""GPU parity of the MX quantiser and the row -> expert map: bit-exact vs the oracle."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from gpu_helpers import dev, host, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _edge_input():
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((12, 128)).astype(np.float32)
+    x[0] = 0.0                                               # all-zero blocks
+    x[1, :32] = np.float32(2.0 ** -120) * rng.standard_normal(32).astype(np.float32)   # clamped scale byte 1
+    x[1, 32:64] = np.float32(1e-40)                          # f32 subnormals
+    x[1, 64:96] = (rng.standard_normal(32) * 1e-39).astype(np.float32)
+    x[2, :32] = np.float32(3.0e38) * np.sign(rng.standard_normal(32)).astype(np.float32)
+    pos = oracle.E4M3_VALUES[:0x7F]
+    mids = (pos[:-1] + pos[1:]) / 2
+    x[3, :32] = 256.0                                        # max sets the scale to 2^0
+    x[3, 1:32] = mids[np.linspace(0, len(mids) - 1, 31).astype(int)]   # exact ties
+    x[4, :32] = np.linspace(-511, 511, 32)                   # saturation
+    x[4, 0] = 300.0
+    x[5, :32] = -0.0
+    x[5, 5] = -1.0
+    x[5, 6] = -2.0 ** -30                                    # rounds to -0
+    x[6] *= 64.0
+    x[7, ::7] *= 1e6
+    return x
+
+
+@pytest.mark.parametrize("case", ["edge", "row32", "odd_rows", "long_rows"])
+def test_quantize_bit_exact(case):
+    torch, mg = require_gpu()
+    rng = np.random.default_rng({"edge": 1, "row32": 2, "odd_rows": 3, "long_rows": 4}[case])
+    if case == "edge":
+        x = _edge_input()
+    elif case == "row32":
+        x = rng.standard_normal((7, 32)).astype(np.float32)
+    elif case == "odd_rows":
+        x = (rng.standard_normal((37, 96)) * np.exp2(rng.integers(-60, 60, (37, 1)))).astype(np.float32)
+    else:
+        x = rng.standard_normal((19, 4096 + 32)).astype(np.float32)
+    say("quantize", case, x.shape)
+    q, s = mg.mx_quantize(dev(torch, x))
+    torch.cuda.synchronize()
+    want_q, want_s = oracle.mx_quantize(x)
+    assert np.array_equal(host(s), want_s)
+    got_q = host(q)
+    bad = np.argwhere(got_q != want_q)
+    assert bad.size == 0, (bad[:5], x[tuple(bad[0])], got_q[tuple(bad[0])], want_q[tuple(bad[0])])
+
+
+@pytest.mark.parametrize("idx", [3, 4])
+def test_quantize_workload_inputs(idx):
+    torch, mg = require_gpu()
+    inp = wl.make_wgrad_inputs(idx)
+    for name in ("gT", "xT"):
+        say("quantize workload", idx, name, inp[name].shape)
+        q, s = mg.mx_quantize(dev(torch, inp[name]))
+        torch.cuda.synchronize()
+        want_q, want_s = oracle.mx_quantize(inp[name])
+        assert np.array_equal(host(s), want_s)
+        assert np.array_equal(host(q), want_q)
+
+
+OFFSETS = [
+    [0, 256],
+    [0, 0, 0, 100, 100, 256],
+    [0, 100, 256, 256, 256],
+    [0, 1, 2, 3, 256],
+    list(range(0, 257, 4)),
+]
+
+
+@pytest.mark.parametrize("off", OFFSETS + ["workload2", "workload5"])
+def test_row_experts_bit_exact(off):
+    torch, mg = require_gpu()
+    if off == "workload2":
+        off = wl.make_offsets(2, np.random.default_rng(2))
+    elif off == "workload5":
+        off = wl.make_offsets(5, np.random.default_rng(5))
+    off = np.asarray(off, np.int32)
+    M = int(off[-1])
+    say("row_experts", off[:6], M)
+    got = host(mg.row_experts(dev(torch, off), M))
+    assert np.array_equal(got, oracle.row_experts(off, M))
