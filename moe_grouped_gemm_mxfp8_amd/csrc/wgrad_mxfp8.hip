@@ -15,14 +15,18 @@
 //    that XCD's L2.
 //  * Each 128-token step stages x^T[256 x 128] and g^T[256 x 128] fp8 (32 KB
 //    each) plus their 256 scale dwords in LDS, with buffer loads that write
-//    LDS directly (no VGPR round trip), double-buffered: step s+1 is in
-//    flight while step s is multiplied.  The 16-byte chunks of each 128-byte
-//    LDS row are XOR-swizzled by (row/2) mod 8 so that the MFMA operand reads
-//    (16 rows x 16 bytes per pass) hit distinct banks.
+//    LDS directly (no VGPR round trip), double-buffered.  A workgroup walks
+//    the steps of all its tiles as one stream: the load of the next step
+//    (possibly the next tile's first) is issued right after the step's
+//    barrier.  (Warming L2 a few steps ahead with one load per line was
+//    measured slower: the extra lines evict operands still in use.)
+//    One barrier per step: it both publishes the step's data and frees the
+//    other buffer.  The 16-byte chunks of each 128-byte LDS row are XOR-
+//    swizzled by (row/2) mod 8 so that the MFMA operand reads (16 rows x 16
+//    bytes per pass) hit distinct banks.
 //  * 8 waves as 2 (k) x 4 (n); each wave owns a 128 x 64 output patch as
 //    4 x 2 accumulators of v_mfma_scale_f32_32x32x64_f8f6f4.  x^T is the
-//    MFMA A operand (rows = k) and g^T the B operand (columns = n), so each
-//    lane ends with 4 consecutive k of one output row n, stored as 8 bytes.
+//    MFMA A operand (rows = k) and g^T the B operand (columns = n).
 //  * Operand lane layout of the scaled MFMA (measured on gfx950, the decode
 //    page's lds_b8 note says the same for 16x16x128): lane l holds row l%32;
 //    lane group g = l/32 holds tokens 16g..16g+15 and 32+16g..32+16g+15 of the
@@ -30,6 +34,10 @@
 //    the half.  The four scale bytes of a row for one 128-token step are one
 //    dword (scales are row-major [rows][M/32]); shifted right by 8g it serves
 //    both halves through op_sel = 0 and 2.
+//  * Epilogue: the bf16 tile goes through LDS (the buffer the tile's last
+//    step has freed) so that each store instruction writes whole 512-byte row
+//    segments; partial-line non-temporal stores measured several times slower.
+//    The stores drain while the next tile's steps run.
 #include "common.hpp"
 #include "../../include/moe_gg.h"
 
@@ -48,7 +56,7 @@ constexpr int ST_G = ST_X + TK * TT;          // g^T tile [256][128] fp8
 constexpr int ST_SX = ST_G + TN * TT;         // x^T scale dwords [256]
 constexpr int ST_SG = ST_SX + TK * 4;         // g^T scale dwords [256]
 constexpr int STAGE_BYTES = ST_SG + TN * 4;   // 67584
-constexpr int DMA_PER_STAGE = 9;              // per wave: 4 + 4 tile chunks, 1 scale chunk
+constexpr int STORES_PER_TILE = 16;           // 16-byte stores per lane per output tile
 
 struct Tile {
   int valid, e, nk, tok0, nt, kt;
@@ -88,6 +96,97 @@ __device__ __forceinline__ uint32_t big_code_mask(uint32_t x) {
   return (m << 1) - (m >> 7);
 }
 
+// One 128-token step of a wave's 128 x 64 patch: 16 block-scaled MFMAs
+// (32 in the two-pass form).  The fragments of both 64-token halves are
+// read from LDS up front and the MFMAs of the first half are interleaved
+// with the reads of the second, so only the first reads' latency is exposed.
+template <bool SPLIT>
+__device__ __forceinline__ void compute_step(const uint8_t *st, v16f (&acc)[4][2], const uint32_t (&xrow)[4],
+                                             const uint32_t (&grow)[2], const uint32_t (&chunk_off)[2][2],
+                                             int wk, int wn, int l32, int g) {
+  uint32_t sx[4], sg[2];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+    sx[a] = *reinterpret_cast<const uint32_t *>(st + ST_SX + 4 * (wk * 128 + a * 32 + l32)) >> (8 * g);
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+    sg[b] = *reinterpret_cast<const uint32_t *>(st + ST_SG + 4 * (wn * 64 + b * 32 + l32)) >> (8 * g);
+  auto frag = [&](uint32_t row, int h) {
+    const v4i lo = *reinterpret_cast<const v4i *>(st + row + chunk_off[h][0]);
+    const v4i hi = *reinterpret_cast<const v4i *>(st + row + chunk_off[h][1]);
+    return (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  };
+  auto mm = [&](int a, int b, const v8i &x, const v8i &gop, int h) {
+    if (h == 0)
+      acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          x, gop, acc[a][b], 0, 0, 0, static_cast<int>(sx[a]), 0, static_cast<int>(sg[b]));
+    else
+      acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          x, gop, acc[a][b], 0, 0, 2, static_cast<int>(sx[a]), 2, static_cast<int>(sg[b]));
+  };
+  // first half: g fragments and x fragments; second half: g fragments early,
+  // each x fragment as soon as the first half's fragment of the same rows is done
+  v8i g0[2], g1[2], x[4];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) g0[b] = frag(grow[b], 0);
+#pragma unroll
+  for (int a = 0; a < 4; ++a) x[a] = frag(xrow[a], 0);
+#pragma unroll
+  for (int b = 0; b < 2; ++b) g1[b] = frag(grow[b], 1);
+  if constexpr (SPLIT) {
+    // two passes: the g^T codes of magnitude >= 128, then the rest, so that no
+    // 8-token run of the MFMA mixes a block's largest codes with its small ones
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      v8i gh[2], gl[2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t v = static_cast<uint32_t>(h == 0 ? g0[b][i] : g1[b][i]);
+          const uint32_t m = big_code_mask(v);
+          gh[b][i] = static_cast<int>(v & m);
+          gl[b][i] = static_cast<int>(v & ~m);
+        }
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        mm(a, 0, x[a], gh[0], h);
+        mm(a, 1, x[a], gh[1], h);
+        mm(a, 0, x[a], gl[0], h);
+        mm(a, 1, x[a], gl[1], h);
+        if (h == 0) x[a] = frag(xrow[a], 1);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      mm(a, 0, x[a], g0[0], 0);
+      mm(a, 1, x[a], g0[1], 0);
+      x[a] = frag(xrow[a], 1);
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      mm(a, 0, x[a], g1[0], 1);
+      mm(a, 1, x[a], g1[1], 1);
+    }
+    // scales and first-half reads, then MFMAs with the second half's x reads between
+    __builtin_amdgcn_sched_group_barrier(0x100, 22, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+  }
+}
+
+// Position in a workgroup's stream of 128-token steps (tiles t = blockIdx.x,
+// blockIdx.x + gridDim.x, ...; tiles of empty experts have no steps).
+struct Cursor {
+  int t, s;
+  Tile ti;
+};
+
 template <bool SPLIT>
 __global__ __launch_bounds__(NTHREAD, 1) void wgrad_mxfp8_kernel(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, uint16_t *__restrict__ C,
@@ -102,6 +201,7 @@ __global__ __launch_bounds__(NTHREAD, 1) void wgrad_mxfp8_kernel(
   const int tilesN = N / TN, tilesK = K / TK;
   const int T = tilesN * tilesK;
   const int total = E * T;
+  const int G = gridDim.x;
 
   // ---- expert ranking: most 128-token steps first, ties by index --------
   {
@@ -158,8 +258,28 @@ __global__ __launch_bounds__(NTHREAD, 1) void wgrad_mxfp8_kernel(
     chunk_off[h][1] = (((4 * h + 2 + g) ^ swz) * 16);
   }
 
-  auto issue_stage = [&](const Tile &ti, int s, uint32_t buf) {
-    const uint32_t tok = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(ti.tok0 + s * TT));
+  auto info = [&](int t) { return tile_info(t, total, T, tilesK, s_order, off, M); };
+  // next position with a step, or t >= total when the stream is done
+  auto advance = [&](Cursor &c) {
+    if (c.s + 1 < c.ti.nk) { ++c.s; return; }
+    c.s = 0;
+    c.t += G;
+    c.ti = info(c.t);
+    while (c.ti.valid && c.ti.nk == 0) { c.t += G; c.ti = info(c.t); }
+  };
+  auto first = [&](int t) {
+    Cursor c;
+    c.t = t; c.s = 0; c.ti = info(t);
+    while (c.ti.valid && c.ti.nk == 0) { c.t += G; c.ti = info(c.t); }
+    return c;
+  };
+
+  int ops = 0;               // vector-memory instructions this wave has issued (uniform)
+  int mark[2] = {0, 0};      // value of ops right after the loads of the step in buffer 0 / 1
+
+  auto issue_stage = [&](const Cursor &c, uint32_t buf) {
+    const Tile &ti = c.ti;
+    const uint32_t tok = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(ti.tok0 + c.s * TT));
     const v4i srd_x = make_srd(B + static_cast<size_t>(ti.kt) * TK * M, TK * Mb);
     const v4i srd_g = make_srd(A + static_cast<size_t>(ti.nt) * TN * M, TN * Mb);
     const uint32_t base = smem_base + buf * STAGE_BYTES;
@@ -175,17 +295,33 @@ __global__ __launch_bounds__(NTHREAD, 1) void wgrad_mxfp8_kernel(
     const v4i srd_s = make_srd(sbase, 256u * scale_row);
     const uint32_t sdst = base + (xs ? ST_SX : ST_SG) + (wave & 3) * 256;
     dma_b32(srd_s, voff_s, tok / 32, __builtin_amdgcn_readfirstlane(sdst));
+    ops += 9;
+  };
+  // wait until the loads of the step in buffer b have landed: every vector
+  // memory instruction issued after them may still be in flight
+  auto wait_step = [&](int b) {
+    const int younger = ops - mark[b];
+    if (younger >= 49) wait_vmcnt<49>();
+    else if (younger >= 33) wait_vmcnt<33>();
+    else if (younger >= 17) wait_vmcnt<17>();
+    else if (younger >= 9) wait_vmcnt<9>();
+    else if (younger >= 1) wait_vmcnt<1>();
+    else wait_vmcnt<0>();
   };
 
-  v16f acc[4][2];
-  int t = blockIdx.x;
-  Tile cur = tile_info(t, total, T, tilesK, s_order, off, M);
-  uint32_t buf = 0;
-  if (cur.valid && cur.nk > 0) issue_stage(cur, 0, buf);
+  // ---- prologue: first step in flight ----
+  Cursor ld = first(blockIdx.x);        // next step to load into LDS
+  uint32_t ld_buf = 0;
+  if (ld.ti.valid) {
+    issue_stage(ld, 0);
+    mark[0] = ops;
+    advance(ld);
+  }
 
-  while (cur.valid) {
-    const int tn = t + gridDim.x;
-    const Tile nxt = tile_info(tn, total, T, tilesK, s_order, off, M);
+  uint32_t buf = 0;                    // buffer of the step being computed
+  v16f acc[4][2];
+  for (int t = blockIdx.x; t < total; t += G) {
+    const Tile cur = info(t);
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -195,98 +331,52 @@ __global__ __launch_bounds__(NTHREAD, 1) void wgrad_mxfp8_kernel(
 
 #pragma unroll 1
     for (int s = 0; s < cur.nk; ++s) {
-      if (s + 1 < cur.nk) {
-        issue_stage(cur, s + 1, buf ^ 1);
-        wait_vmcnt<DMA_PER_STAGE>();
-      } else {
-        wait_vmcnt<0>();
-      }
+      wait_step(buf);
       barrier();
+      ld_buf = buf ^ 1;
+      if (ld.ti.valid) {
+        issue_stage(ld, ld_buf);
+        mark[ld_buf] = ops;
+        advance(ld);
+      }
+
       const uint8_t *st = smem + buf * STAGE_BYTES;
-      uint32_t sx[4], sg[2];
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-        sx[a] = *reinterpret_cast<const uint32_t *>(st + ST_SX + 4 * (wk * 128 + a * 32 + l32)) >> (8 * g);
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-        sg[b] = *reinterpret_cast<const uint32_t *>(st + ST_SG + 4 * (wn * 64 + b * 32 + l32)) >> (8 * g);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        v8i xa[4], gb[2];
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const v4i lo = *reinterpret_cast<const v4i *>(st + xrow[a] + chunk_off[h][0]);
-          const v4i hi = *reinterpret_cast<const v4i *>(st + xrow[a] + chunk_off[h][1]);
-          xa[a] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          const v4i lo = *reinterpret_cast<const v4i *>(st + grow[b] + chunk_off[h][0]);
-          const v4i hi = *reinterpret_cast<const v4i *>(st + grow[b] + chunk_off[h][1]);
-          gb[b] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          v8i gop = gb[b];
-          if (SPLIT) {
-            // pass 1: the g^T codes of magnitude >= 128; pass 2 (below): the rest
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-              gop[i] = static_cast<int>(static_cast<uint32_t>(gb[b][i]) & big_code_mask(static_cast<uint32_t>(gb[b][i])));
-          }
-#pragma unroll
-          for (int a = 0; a < 4; ++a) {
-            if (h == 0)
-              acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                  xa[a], gop, acc[a][b], 0, 0, 0, static_cast<int>(sx[a]), 0, static_cast<int>(sg[b]));
-            else
-              acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                  xa[a], gop, acc[a][b], 0, 0, 2, static_cast<int>(sx[a]), 2, static_cast<int>(sg[b]));
-          }
-          if (SPLIT) {
-            v8i glo;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) glo[i] = gb[b][i] ^ gop[i];
-#pragma unroll
-            for (int a = 0; a < 4; ++a) {
-              if (h == 0)
-                acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    xa[a], glo, acc[a][b], 0, 0, 0, static_cast<int>(sx[a]), 0, static_cast<int>(sg[b]));
-              else
-                acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    xa[a], glo, acc[a][b], 0, 0, 2, static_cast<int>(sx[a]), 2, static_cast<int>(sg[b]));
-            }
-          }
-        }
-      }
-      barrier();
+      compute_step<SPLIT>(st, acc, xrow, grow, chunk_off, wk, wn, l32, g);
       buf ^= 1;
     }
 
-    // every wave is past its last read of both stage buffers: start the next tile's first step
-    if (nxt.valid && nxt.nk > 0) issue_stage(nxt, 0, buf);
-
-    const size_t crow0 = static_cast<size_t>(cur.e) * N + static_cast<size_t>(cur.nt) * TN;
-    const int ccol0 = cur.kt * TK;
+    // ---- epilogue from registers -------------------------------------------
+    // the output tile: 256 rows of K bf16 from (e*N + nt*256, kt*256); 32-bit offsets inside it
+    uint16_t *const ctile = C + (static_cast<size_t>(cur.e) * N + static_cast<size_t>(cur.nt) * TN) * K +
+                            static_cast<size_t>(cur.kt) * TK;
+    const uint32_t Ku = static_cast<uint32_t>(K);
     if (cur.nk == 0) {
-      // empty expert: +0.0 everywhere, written as whole 512-byte row segments
+      // empty expert: +0.0 everywhere, whole 512-byte row segments
       const v4i z = {0, 0, 0, 0};
-#pragma unroll 4
-      for (int p = 0; p < TN / 16; ++p) {
+#pragma unroll
+      for (int p = 0; p < STORES_PER_TILE; ++p) {
         const int row = p * 16 + (tid >> 5);
-        __builtin_nontemporal_store(z, reinterpret_cast<v4i *>(C + (crow0 + row) * K + ccol0 + (tid & 31) * 8));
+        __builtin_nontemporal_store(z, reinterpret_cast<v4i *>(ctile + (static_cast<uint32_t>(row) * Ku + (tid & 31) * 8)));
       }
     } else {
-      // ---- epilogue through LDS: bf16 tile rows of 512 bytes, stored whole ----
-      // staging row r (of 128) holds output row crow0 + half*128 + r; its 16-byte
-      // chunks are XOR-swizzled by (r mod 32) so the 8-byte writes of 32 rows spread
+      // staging through LDS in the buffer of the tile's last step (the other
+      // buffer already holds the next step in flight): staging row r (of 128)
+      // is output row crow0 + half*128 + r, its 16-byte chunks XOR-swizzled by
+      // (r mod 32); each half is then stored as whole 512-byte row segments
       uint8_t *stg = smem + (buf ^ 1) * STAGE_BYTES;
+      // recompute the lane coordinates here rather than keep them live across
+      // the step loop (spilled addresses would be reloaded with a vmcnt wait
+      // that drains the next step's loads)
+      int etid = tid;
+      asm volatile("" : "+v"(etid));
+      const int el32 = etid & 31, eg = (etid >> 5) & 1;
+      barrier();                                   // all waves are done reading that buffer
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         if ((wn >> 1) == half) {
 #pragma unroll
           for (int b = 0; b < 2; ++b) {
-            const int r = (wn & 1) * 64 + b * 32 + l32;
+            const int r = (wn & 1) * 64 + b * 32 + el32;
 #pragma unroll
             for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -295,23 +385,24 @@ __global__ __launch_bounds__(NTHREAD, 1) void wgrad_mxfp8_kernel(
                 const uint32_t lo = pack_bf16x2(acc[a][b][4 * q + 0], acc[a][b][4 * q + 1]);
                 const uint32_t hi = pack_bf16x2(acc[a][b][4 * q + 2], acc[a][b][4 * q + 3]);
                 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
-                *reinterpret_cast<u2 *>(stg + r * 512 + ((c ^ (r & 31)) << 4) + 8 * g) = (u2){lo, hi};
+                *reinterpret_cast<u2 *>(stg + r * 512 + ((c ^ (r & 31)) << 4) + 8 * eg) = (u2){lo, hi};
               }
           }
         }
         barrier();
 #pragma unroll
         for (int p = 0; p < 8; ++p) {
-          const int r = p * 16 + (tid >> 5);
-          const int c = tid & 31;
+          const int r = p * 16 + (etid >> 5);
+          const int c = etid & 31;
           const v4i v = *reinterpret_cast<const v4i *>(stg + r * 512 + ((c ^ (r & 31)) << 4));
-          __builtin_nontemporal_store(v, reinterpret_cast<v4i *>(C + (crow0 + half * 128 + r) * K + ccol0 + c * 8));
+          __builtin_nontemporal_store(v, reinterpret_cast<v4i *>(ctile + (static_cast<uint32_t>(half * 128 + r) * Ku + c * 8)));
         }
-        barrier();
+        // the second half overwrites the staging; after it, the next step's
+        // barrier precedes any load into this buffer
+        if (half == 0) barrier();
       }
     }
-    t = tn;
-    cur = nxt;
+    ops += STORES_PER_TILE;
   }
   wait_vmcnt<0>();
 }
