@@ -231,12 +231,27 @@ def bench_quantize(torch, mg, idx, steps, warmup, cpu_baseline):
     return line
 
 
+def bench_copy(torch, mg, idx, steps, warmup, cpu_baseline):
+    """A plain device copy of a known size: calibrates the FETCH_SIZE / WRITE_SIZE counters."""
+    nbytes = 1 << 30
+    d = torch.device("cuda:0")
+    src = torch.empty(nbytes, dtype=torch.uint8, device=d).fill_(1)
+    dst = torch.empty_like(src)
+    ms = time_steps(torch, lambda: dst.copy_(src), steps, warmup)
+    gbs = 2 * nbytes / (ms * 1e-3) / 1e9
+    return {"metric": "GB/s, device copy of 1 GiB (counter calibration)", "value": round(gbs, 1),
+            "unit": "GB/s", "ms_per_step": round(ms, 4), "dtype": "u8",
+            "config": {"workload": "copy_1GiB", "bytes": nbytes},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": 2 * nbytes}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--pass", dest="pass_name", choices=["wgrad", "dgrad", "quantize"], default="wgrad")
+    ap.add_argument("--pass", dest="pass_name", choices=["wgrad", "dgrad", "quantize", "copy"], default="wgrad")
     ap.add_argument("--workload", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fast", action="store_true", help="wgrad: the single-pass entry point")
@@ -253,14 +268,15 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
 
-    idx = args.workload or {"wgrad": 4, "dgrad": 5, "quantize": 4}[args.pass_name]
-    fn = {"wgrad": bench_wgrad, "dgrad": bench_dgrad, "quantize": bench_quantize}[args.pass_name]
+    idx = args.workload or {"wgrad": 4, "dgrad": 5, "quantize": 4, "copy": 0}[args.pass_name]
+    fn = {"wgrad": bench_wgrad, "dgrad": bench_dgrad, "quantize": bench_quantize, "copy": bench_copy}[args.pass_name]
     kw = {"fast": True} if (args.fast and args.pass_name == "wgrad") else {}
     line = fn(torch, mg, idx, args.steps, args.warmup, not args.no_cpu_baseline, **kw)
     line.update({"n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
                  "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
                  "data": "synthetic (seeded numpy generators, workload recipe)",
-                 "kernel": KERNEL_NAMES[args.pass_name], "kernel_source_digest": source_digest(args.pass_name)})
+                 "kernel": KERNEL_NAMES.get(args.pass_name, "torch copy"),
+                 "kernel_source_digest": source_digest(args.pass_name) if args.pass_name in KERNEL_SOURCES else None})
     print(json.dumps(line), flush=True)
 
 

@@ -135,7 +135,8 @@ __device__ __forceinline__ void compute_step(const uint8_t *st, v16f (&acc)[4][2
   for (int b = 0; b < 2; ++b) g1[b] = frag(grow[b], 1);
   if constexpr (SPLIT) {
     // two passes: the g^T codes of magnitude >= 128, then the rest, so that no
-    // 8-token run of the MFMA mixes a block's largest codes with its small ones
+    // 8-token run of the MFMA mixes a block's largest codes with its small ones.
+    // The passes over one accumulator are 8 MFMAs apart (no result-latency stall).
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       v8i gh[2], gl[2];
@@ -152,6 +153,9 @@ __device__ __forceinline__ void compute_step(const uint8_t *st, v16f (&acc)[4][2
       for (int a = 0; a < 4; ++a) {
         mm(a, 0, x[a], gh[0], h);
         mm(a, 1, x[a], gh[1], h);
+      }
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
         mm(a, 0, x[a], gl[0], h);
         mm(a, 1, x[a], gl[1], h);
         if (h == 0) x[a] = frag(xrow[a], 1);
@@ -346,17 +350,21 @@ __global__ __launch_bounds__(NTHREAD, 1) void wgrad_mxfp8_kernel(
     }
 
     // ---- epilogue from registers -------------------------------------------
-    // the output tile: 256 rows of K bf16 from (e*N + nt*256, kt*256); 32-bit offsets inside it
-    uint16_t *const ctile = C + (static_cast<size_t>(cur.e) * N + static_cast<size_t>(cur.nt) * TN) * K +
-                            static_cast<size_t>(cur.kt) * TK;
+    // the output tile: 256 rows of K bf16 from (e*N + nt*256, kt*256), written
+    // through a buffer descriptor with 32-bit byte offsets (non-temporal)
     const uint32_t Ku = static_cast<uint32_t>(K);
+    const __amdgpu_buffer_rsrc_t crsrc = __builtin_amdgcn_make_buffer_rsrc(
+        C + (static_cast<size_t>(cur.e) * N + static_cast<size_t>(cur.nt) * TN) * K + static_cast<size_t>(cur.kt) * TK,
+        static_cast<short>(0), static_cast<int>(TN * Ku * 2u), 0x00020000);
     if (cur.nk == 0) {
       // empty expert: +0.0 everywhere, whole 512-byte row segments
-      const v4i z = {0, 0, 0, 0};
+      int etid = tid;
+      asm volatile("" : "+v"(etid));
+      const v4u z = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int p = 0; p < STORES_PER_TILE; ++p) {
-        const int row = p * 16 + (tid >> 5);
-        __builtin_nontemporal_store(z, reinterpret_cast<v4i *>(ctile + (static_cast<uint32_t>(row) * Ku + (tid & 31) * 8)));
+        const uint32_t row = static_cast<uint32_t>(p * 16 + (etid >> 5));
+        __builtin_amdgcn_raw_buffer_store_b128(z, crsrc, static_cast<int>((row * Ku + (etid & 31) * 8) * 2u), 0, 2);
       }
     } else {
       // staging through LDS in the buffer of the tile's last step (the other
@@ -394,8 +402,9 @@ __global__ __launch_bounds__(NTHREAD, 1) void wgrad_mxfp8_kernel(
         for (int p = 0; p < 8; ++p) {
           const int r = p * 16 + (etid >> 5);
           const int c = etid & 31;
-          const v4i v = *reinterpret_cast<const v4i *>(stg + r * 512 + ((c ^ (r & 31)) << 4));
-          __builtin_nontemporal_store(v, reinterpret_cast<v4i *>(ctile + (static_cast<uint32_t>(half * 128 + r) * Ku + c * 8)));
+          const v4u v = *reinterpret_cast<const v4u *>(stg + r * 512 + ((c ^ (r & 31)) << 4));
+          __builtin_amdgcn_raw_buffer_store_b128(
+              v, crsrc, static_cast<int>((static_cast<uint32_t>(half * 128 + r) * Ku + c * 8) * 2u), 0, 2);
         }
         // the second half overwrites the staging; after it, the next step's
         // barrier precedes any load into this buffer
