@@ -249,8 +249,8 @@ def bench_copy(torch, mg, idx, steps, warmup, cpu_baseline):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--pass", dest="pass_name", choices=["wgrad", "dgrad", "quantize", "copy"], default="wgrad")
     ap.add_argument("--workload", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -21,9 +21,11 @@
 //    barrier.  (Warming L2 a few steps ahead with one load per line was
 //    measured slower: the extra lines evict operands still in use.)
 //    One barrier per step: it both publishes the step's data and frees the
-//    other buffer.  The 16-byte chunks of each 128-byte LDS row are XOR-
-//    swizzled by (row/2) mod 8 so that the MFMA operand reads (16 rows x 16
-//    bytes per pass) hit distinct banks.
+//    other buffer.  An operand tile in LDS is 32 blocks of 8 rows x 128
+//    bytes, each block padded by 16 bytes; a load instruction fills one
+//    block, eight lanes per row reading the row's 128 bytes in order (whole
+//    lines, no permuted lanes), and rows are placed so that the 16 rows an
+//    MFMA operand read touches at once fall on 16 distinct bank groups.
 //  * 8 waves as 2 (k) x 4 (n); each wave owns a 128 x 64 output patch as
 //    4 x 2 accumulators of v_mfma_scale_f32_32x32x64_f8f6f4.  x^T is the
 //    MFMA A operand (rows = k) and g^T the B operand (columns = n).
@@ -51,16 +53,25 @@ constexpr int NWAVE = 8;
 constexpr int NTHREAD = NWAVE * 64;
 constexpr int MAX_EXPERTS = 1024;
 
-constexpr int ST_X = 0;                       // x^T tile [256][128] fp8
-constexpr int ST_G = ST_X + TK * TT;          // g^T tile [256][128] fp8
-constexpr int ST_SX = ST_G + TN * TT;         // x^T scale dwords [256]
+// Row r of a 64-row group G = r/64 sits in block 8G + r%8 at slot (r%64)/8.
+constexpr int BLK = 8 * TT + 16;              // 1040: 8 rows of 128 bytes + padding
+constexpr int TILE_BYTES = 32 * BLK;          // 33280: a 256-row operand tile
+constexpr int ST_X = 0;                       // x^T tile
+constexpr int ST_G = ST_X + TILE_BYTES;       // g^T tile
+constexpr int ST_SX = ST_G + TILE_BYTES;      // x^T scale dwords [256]
 constexpr int ST_SG = ST_SX + TK * 4;         // g^T scale dwords [256]
-constexpr int STAGE_BYTES = ST_SG + TN * 4;   // 67584
+constexpr int STAGE_BYTES = ST_SG + TN * 4;   // 68608
+static_assert(128 * 512 <= STAGE_BYTES, "the epilogue stages 128 rows of 512 bytes in one buffer");
 constexpr int STORES_PER_TILE = 16;           // 16-byte stores per lane per output tile
 
 struct Tile {
   int valid, e, nk, tok0, nt, kt;
 };
+
+// LDS byte offset of row r (0..255) inside an operand tile.
+__device__ __forceinline__ uint32_t tile_row(int r) {
+  return static_cast<uint32_t>(((r >> 6) * 8 + (r & 7)) * BLK + ((r & 63) >> 3) * TT);
+}
 
 __device__ __forceinline__ Tile tile_info(int t, int total, int T, int tilesK, const int *s_order,
                                           const int32_t *__restrict__ off, int M) {
@@ -232,15 +243,15 @@ __global__ __launch_bounds__(NTHREAD, 1) void wgrad_mxfp8_kernel(
   const uint32_t smem_base = lds_addr(smem);
   const uint32_t Mb = static_cast<uint32_t>(M);
   const uint32_t scale_row = Mb / 32;      // bytes per scale row
-  // tile DMA: wave w fills 1 KB chunks 4w..4w+3 of each operand tile; chunk q
-  // holds tile rows 8q..8q+7, lane L -> row 8q + L/8, LDS slot L%8, which
-  // takes the row's global 16-byte chunk (L%8) ^ ((row/2) mod 8).
+  // tile DMA: wave w fills blocks 4w..4w+3 of each operand tile; block
+  // 8G + q holds rows 64G + 8j + q (slot j), lane L -> slot L/8, bytes
+  // 16(L%8)..16(L%8)+15 of the row's 128-token step.
   uint32_t voff_t[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int r = 8 * (wave * 4 + i) + (lane >> 3);
-    const int c = (lane & 7) ^ ((r >> 1) & 7);
-    voff_t[i] = static_cast<uint32_t>(r) * Mb + static_cast<uint32_t>(c) * 16u;
+    const int blk = wave * 4 + i;
+    const int r = 64 * (blk >> 3) + 8 * (lane >> 3) + (blk & 7);
+    voff_t[i] = static_cast<uint32_t>(r) * Mb + static_cast<uint32_t>(lane & 7) * 16u;
   }
   // scale DMA: waves 0-3 load x^T scale rows, waves 4-7 g^T scale rows, 64 rows each
   const int srow = (wave & 3) * 64 + lane;
@@ -249,17 +260,16 @@ __global__ __launch_bounds__(NTHREAD, 1) void wgrad_mxfp8_kernel(
   // MFMA operand addressing
   const int wk = wave >> 2, wn = wave & 3;
   const int g = lane >> 5, l32 = lane & 31;
-  const int swz = (l32 >> 1) & 7;
   uint32_t xrow[4], grow[2];
 #pragma unroll
-  for (int a = 0; a < 4; ++a) xrow[a] = ST_X + (wk * 128 + a * 32 + l32) * TT;
+  for (int a = 0; a < 4; ++a) xrow[a] = ST_X + tile_row(wk * 128 + a * 32 + l32);
 #pragma unroll
-  for (int b = 0; b < 2; ++b) grow[b] = ST_G + (wn * 64 + b * 32 + l32) * TT;
-  uint32_t chunk_off[2][2];   // [half][piece] -> swizzled 16-byte chunk offset
+  for (int b = 0; b < 2; ++b) grow[b] = ST_G + tile_row(wn * 64 + b * 32 + l32);
+  uint32_t chunk_off[2][2];   // [half][piece] -> 16-byte chunk offset within the row
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    chunk_off[h][0] = (((4 * h + g) ^ swz) * 16);
-    chunk_off[h][1] = (((4 * h + 2 + g) ^ swz) * 16);
+    chunk_off[h][0] = (4 * h + g) * 16;
+    chunk_off[h][1] = (4 * h + 2 + g) * 16;
   }
 
   auto info = [&](int t) { return tile_info(t, total, T, tilesK, s_order, off, M); };
@@ -289,10 +299,10 @@ __global__ __launch_bounds__(NTHREAD, 1) void wgrad_mxfp8_kernel(
     const uint32_t base = smem_base + buf * STAGE_BYTES;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      dma_b128(srd_x, voff_t[i], tok, __builtin_amdgcn_readfirstlane(base + ST_X + (wave * 4 + i) * 1024));
+      dma_b128(srd_x, voff_t[i], tok, __builtin_amdgcn_readfirstlane(base + ST_X + (wave * 4 + i) * BLK));
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      dma_b128(srd_g, voff_t[i], tok, __builtin_amdgcn_readfirstlane(base + ST_G + (wave * 4 + i) * 1024));
+      dma_b128(srd_g, voff_t[i], tok, __builtin_amdgcn_readfirstlane(base + ST_G + (wave * 4 + i) * BLK));
     const bool xs = wave < 4;
     const uint8_t *sbase = xs ? SB + static_cast<size_t>(ti.kt) * TK * scale_row
                               : SA + static_cast<size_t>(ti.nt) * TN * scale_row;
