@@ -101,10 +101,13 @@ __device__ __forceinline__ Tile tile_info(int t, int total, int T, int tilesK, c
 }
 
 // Byte mask of the E4M3 codes in a dword whose magnitude is >= 128
-// (exponent field >= 14): 0xFF in those bytes, 0x00 elsewhere.
+// (exponent field >= 14): 0xFF in those bytes, 0x00 elsewhere.  Bit 7 of
+// each byte of y flags such a code; v_perm_b32 selectors 8-11 broadcast the
+// top bit of bytes 1 and 3 of each source, so y supplies bytes 1 and 3 and
+// y << 8 bytes 0 and 2.
 __device__ __forceinline__ uint32_t big_code_mask(uint32_t x) {
-  const uint32_t m = ((x & 0x70707070u) + 0x10101010u) & 0x80808080u;
-  return (m << 1) - (m >> 7);
+  const uint32_t y = (x & 0x70707070u) + 0x10101010u;
+  return __builtin_amdgcn_perm(y << 8, y, 0x090B080Au);
 }
 
 // One 128-token step of a wave's 128 x 64 patch: 16 block-scaled MFMAs
