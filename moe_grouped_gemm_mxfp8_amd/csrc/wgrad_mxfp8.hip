@@ -63,6 +63,7 @@ constexpr int ST_SG = ST_SX + TK * 4;         // g^T scale dwords [256]
 constexpr int STAGE_BYTES = ST_SG + TN * 4;   // 68608
 static_assert(128 * 512 <= STAGE_BYTES, "the epilogue stages 128 rows of 512 bytes in one buffer");
 constexpr int STORES_PER_TILE = 16;           // 16-byte stores per lane per output tile
+constexpr int LOADS_PER_STEP = 18;            // stage loads a loading wave issues per step
 
 struct Tile {
   int valid, e, nk, tok0, nt, kt;
@@ -246,19 +247,22 @@ __global__ __launch_bounds__(NTHREAD, 1) void wgrad_mxfp8_kernel(
   const uint32_t smem_base = lds_addr(smem);
   const uint32_t Mb = static_cast<uint32_t>(M);
   const uint32_t scale_row = Mb / 32;      // bytes per scale row
-  // tile DMA: wave w fills blocks 4w..4w+3 of each operand tile; block
-  // 8G + q holds rows 64G + 8j + q (slot j), lane L -> slot L/8, bytes
-  // 16(L%8)..16(L%8)+15 of the row's 128-token step.
-  uint32_t voff_t[4];
+  // Stage loads are issued by waves 4-7 only: a wave blocks while the
+  // address FIFO is full, and so the other wave on each SIMD (0-3) starts
+  // its MFMAs right after the barrier instead of waiting behind its loads.
+  // Wave 4 + w4 fills blocks 8w4..8w4+7 of both operand tiles; block 8G + q
+  // holds rows 64G + 8j + q (slot j), lane L -> slot L/8, bytes
+  // 16(L%8)..16(L%8)+15 of the row's 128-token step; and the scale dwords of
+  // rows 64w4..64w4+63 of both operands.
+  const bool loader = wave >= 4;
+  const int w4 = wave & 3;
+  uint32_t voff_t[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int blk = wave * 4 + i;
-    const int r = 64 * (blk >> 3) + 8 * (lane >> 3) + (blk & 7);
+  for (int i = 0; i < 8; ++i) {
+    const int r = 64 * w4 + 8 * (lane >> 3) + i;
     voff_t[i] = static_cast<uint32_t>(r) * Mb + static_cast<uint32_t>(lane & 7) * 16u;
   }
-  // scale DMA: waves 0-3 load x^T scale rows, waves 4-7 g^T scale rows, 64 rows each
-  const int srow = (wave & 3) * 64 + lane;
-  const uint32_t voff_s = static_cast<uint32_t>(srow) * scale_row;
+  const uint32_t voff_s = static_cast<uint32_t>(w4 * 64 + lane) * scale_row;
 
   // MFMA operand addressing
   const int wk = wave >> 2, wn = wave & 3;
@@ -295,34 +299,33 @@ __global__ __launch_bounds__(NTHREAD, 1) void wgrad_mxfp8_kernel(
   int mark[2] = {0, 0};      // value of ops right after the loads of the step in buffer 0 / 1
 
   auto issue_stage = [&](const Cursor &c, uint32_t buf) {
+    if (!loader) return;
     const Tile &ti = c.ti;
     const uint32_t tok = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(ti.tok0 + c.s * TT));
     const v4i srd_x = make_srd(B + static_cast<size_t>(ti.kt) * TK * M, TK * Mb);
     const v4i srd_g = make_srd(A + static_cast<size_t>(ti.nt) * TN * M, TN * Mb);
     const uint32_t base = smem_base + buf * STAGE_BYTES;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      dma_b128(srd_x, voff_t[i], tok, __builtin_amdgcn_readfirstlane(base + ST_X + (wave * 4 + i) * BLK));
+    for (int i = 0; i < 8; ++i)
+      dma_b128(srd_x, voff_t[i], tok, __builtin_amdgcn_readfirstlane(base + ST_X + (w4 * 8 + i) * BLK));
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      dma_b128(srd_g, voff_t[i], tok, __builtin_amdgcn_readfirstlane(base + ST_G + (wave * 4 + i) * BLK));
-    const bool xs = wave < 4;
-    const uint8_t *sbase = xs ? SB + static_cast<size_t>(ti.kt) * TK * scale_row
-                              : SA + static_cast<size_t>(ti.nt) * TN * scale_row;
-    const v4i srd_s = make_srd(sbase, 256u * scale_row);
-    const uint32_t sdst = base + (xs ? ST_SX : ST_SG) + (wave & 3) * 256;
-    dma_b32(srd_s, voff_s, tok / 32, __builtin_amdgcn_readfirstlane(sdst));
-    ops += 9;
+    for (int i = 0; i < 8; ++i)
+      dma_b128(srd_g, voff_t[i], tok, __builtin_amdgcn_readfirstlane(base + ST_G + (w4 * 8 + i) * BLK));
+    const v4i srd_sx = make_srd(SB + static_cast<size_t>(ti.kt) * TK * scale_row, 256u * scale_row);
+    const v4i srd_sg = make_srd(SA + static_cast<size_t>(ti.nt) * TN * scale_row, 256u * scale_row);
+    dma_b32(srd_sx, voff_s, tok / 32, __builtin_amdgcn_readfirstlane(base + ST_SX + w4 * 256));
+    dma_b32(srd_sg, voff_s, tok / 32, __builtin_amdgcn_readfirstlane(base + ST_SG + w4 * 256));
+    ops += LOADS_PER_STEP;
   };
   // wait until the loads of the step in buffer b have landed: every vector
   // memory instruction issued after them may still be in flight
   auto wait_step = [&](int b) {
     const int younger = ops - mark[b];
-    if (younger >= 49) wait_vmcnt<49>();
-    else if (younger >= 33) wait_vmcnt<33>();
-    else if (younger >= 17) wait_vmcnt<17>();
-    else if (younger >= 9) wait_vmcnt<9>();
-    else if (younger >= 1) wait_vmcnt<1>();
+    if (younger >= 50) wait_vmcnt<50>();
+    else if (younger >= 34) wait_vmcnt<34>();
+    else if (younger >= 18) wait_vmcnt<18>();
+    else if (younger >= 16) wait_vmcnt<16>();
+    else if (younger >= 8) wait_vmcnt<8>();
     else wait_vmcnt<0>();
   };
 
