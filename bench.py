@@ -41,8 +41,10 @@ KERNEL_SOURCES = {
     "wgrad": ["wgrad_mxfp8.hip", "common.hpp"],
     "dgrad": ["dgrad_f32.hip", "common.hpp"],
     "quantize": ["mx_quantize.hip", "common.hpp"],
+    "quantize_t": ["mx_quantize.hip", "common.hpp"],
 }
-KERNEL_NAMES = {"wgrad": "wgrad_mxfp8_kernel", "dgrad": "dgrad_f32_kernel", "quantize": "mx_quantize_kernel"}
+KERNEL_NAMES = {"wgrad": "wgrad_mxfp8_kernel", "dgrad": "dgrad_f32_kernel", "quantize": "mx_quantize_kernel",
+                "quantize_t": "mx_quantize_t_kernel"}
 
 
 def source_digest(pass_name: str) -> str:
@@ -231,6 +233,35 @@ def bench_quantize(torch, mg, idx, steps, warmup, cpu_baseline):
     return line
 
 
+def bench_quantize_t(torch, mg, idx, steps, warmup, cpu_baseline):
+    """The transposing quantiser on g [M, N] -> g^T codes [N, M] (the weight gradient's A operand)."""
+    inp = wl.make_wgrad_inputs(idx)
+    d = torch.device("cuda:0")
+    g = torch.from_numpy(inp["gT"]).to(d).t().contiguous()           # [M, N] token rows
+    del inp
+    R, L = g.shape
+    q = torch.empty((L, R), dtype=torch.uint8, device=d)
+    s = torch.empty((L, R // 32), dtype=torch.uint8, device=d)
+    ms = time_steps(torch, lambda: mg.mx_quantize_t(g, q, s), steps, warmup)
+    nbytes = 4 * R * L + R * L + R * L // 32
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    line = {"metric": f"GB/s, transposing MX quantise of g, workload {idx}", "value": round(gbs, 1), "unit": "GB/s",
+            "ms_per_step": round(ms, 4), "dtype": "f32->e4m3+e8m0",
+            "config": {"workload": wl.WORKLOADS[idx].name, "R": R, "L": L},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": read_traffic("quantize_t", idx)}}
+    if cpu_baseline:
+        import oracle
+        sub = g[:, : max(32, L // 8)].cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.mx_quantize(np.ascontiguousarray(sub.T))
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": round(5.03125 * sub.size / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+                                "kind": "oracle", "seconds": round(dt, 2), "cpu": cpu_info(),
+                                "sample": f"features 0..{sub.shape[1]} of g (oracle.mx_quantize of the transpose)"}
+    return line
+
+
 def bench_copy(torch, mg, idx, steps, warmup, cpu_baseline):
     """A plain device copy of a known size: calibrates the FETCH_SIZE / WRITE_SIZE counters."""
     nbytes = 1 << 30
@@ -251,7 +282,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--pass", dest="pass_name", choices=["wgrad", "dgrad", "quantize", "copy"], default="wgrad")
+    ap.add_argument("--pass", dest="pass_name", choices=["wgrad", "dgrad", "quantize", "quantize_t", "copy"], default="wgrad")
     ap.add_argument("--workload", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fast", action="store_true", help="wgrad: the single-pass entry point")
@@ -268,8 +299,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
 
-    idx = args.workload or {"wgrad": 4, "dgrad": 5, "quantize": 4, "copy": 0}[args.pass_name]
-    fn = {"wgrad": bench_wgrad, "dgrad": bench_dgrad, "quantize": bench_quantize, "copy": bench_copy}[args.pass_name]
+    idx = args.workload or {"wgrad": 4, "dgrad": 5, "quantize": 4, "quantize_t": 4, "copy": 0}[args.pass_name]
+    fn = {"wgrad": bench_wgrad, "dgrad": bench_dgrad, "quantize": bench_quantize, "quantize_t": bench_quantize_t,
+          "copy": bench_copy}[args.pass_name]
     kw = {"fast": True} if (args.fast and args.pass_name == "wgrad") else {}
     line = fn(torch, mg, idx, args.steps, args.warmup, not args.no_cpu_baseline, **kw)
     line.update({"n_gpus": 1, "steps": args.steps, "warmup": args.warmup,

@@ -7,6 +7,7 @@ memory and the current stream, nothing else):
   wgrad_mxfp8(a, b, scale_a, scale_b, expert_off, out=None, fast=False) -> bf16 [E*N, K]
   dgrad_f32(g, w, expert_off, out=None)                     -> f32 [M, K]
   mx_quantize(x, q=None, s=None)                            -> (uint8 [R, L], uint8 [R, L/32])
+  mx_quantize_t(x, q=None, s=None)                          -> (uint8 [L, R], uint8 [L, R/32])
   row_experts(expert_off, M, out=None)                      -> int32 [M]
 
 There is no CPU fallback: calling any of them without the built library or
@@ -15,7 +16,7 @@ without a GPU raises.
 from __future__ import annotations
 
 from ._lib import EINVAL, ELAUNCH, EUNSUPPORTED, OK, MoeGGError, status_string
-from .ops import dgrad_f32, mx_quantize, row_experts, wgrad_mxfp8
+from .ops import dgrad_f32, mx_quantize, mx_quantize_t, row_experts, wgrad_mxfp8
 
-__all__ = ["wgrad_mxfp8", "dgrad_f32", "mx_quantize", "row_experts", "status_string",
+__all__ = ["wgrad_mxfp8", "dgrad_f32", "mx_quantize", "mx_quantize_t", "row_experts", "status_string",
            "MoeGGError", "OK", "EINVAL", "EUNSUPPORTED", "ELAUNCH"]

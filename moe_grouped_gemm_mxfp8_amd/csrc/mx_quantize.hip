@@ -8,18 +8,27 @@
 // E4M3, ties to even, saturating at +-448 (the decode page's mx8_q clamps to
 // +-FP8_MAX before its conversion), sign of zero kept.
 //
-// The rounding is done on the integer fields of the f32 input: the division
-// by a power of two only moves the exponent, so the E4M3 code follows from
-// the 24-bit significand shifted to the target quantum with a round-to-
-// nearest-even on the dropped bits.  That is exact for every finite input,
-// including f32 subnormals and scaled values below E4M3's subnormal range,
-// and independent of the hardware's denormal mode.
+// The E4M3 rounding is the hardware's: v_cvt_pk_fp8_f32 rounds to nearest
+// even, keeps the sign of zero and produces E4M3 subnormals, and matches the
+// oracle code for code on every value up to 464 (measured on gfx950); above
+// that it returns NaN, so the scaled value is first clamped to +-448.  The
+// division by the scale is a multiplication by an exact power of two; only
+// results far below E4M3's subnormal range can lose bits, and those round to
+// a signed zero either way.
 //
-// HBM-bound streaming kernel: rows never split a block (L % 32 == 0), so the
-// [R][L] input is a flat sequence of blocks.  A wave handles 512 elements per
-// step as two coalesced 1 KB float4 sweeps; the 8 lanes that share a block
-// reduce its max with xor shuffles; each lane writes its 4 codes as one dword
-// and the first lane of each block the scale byte.
+// mx_quantize: HBM-bound streaming kernel; rows never split a block (L % 32
+// == 0), so the [R][L] input is a flat sequence of blocks.  A wave handles 512
+// elements per step as two coalesced 1 KB float4 sweeps; the 8 lanes that
+// share a block reduce its max with xor shuffles; each lane writes its 4 codes
+// as one dword and the first lane of each block the scale byte.
+//
+// mx_quantize_t: the same codes for the transpose, so that g [M][N] (tokens x
+// features) becomes g^T codes [N][M] with one scale per 32 tokens without a
+// separate transpose pass.  A 256-thread workgroup takes 128 tokens x 64
+// features: coalesced float4 loads of the token rows into an LDS tile held
+// feature-major, then one thread per (feature, 32-token block) computes the
+// block's scale and writes its 32 codes as two 16-byte stores, four threads
+// covering a feature row's 128 bytes.
 #include "common.hpp"
 #include "../../include/moe_gg.h"
 
@@ -38,39 +47,16 @@ __device__ __forceinline__ uint32_t scale_byte(uint32_t amax_bits) {
   return static_cast<uint32_t>(s < 1 ? 1 : (s > 254 ? 254 : s));
 }
 
-// E4M3 code of x * 2^(127 - sb), round to nearest even, saturating.
-__device__ __forceinline__ uint32_t e4m3_code(float x, int sb) {
-  const uint32_t bits = __float_as_uint(x);
-  const uint32_t sign = (bits >> 24) & 0x80u;
-  const uint32_t a = bits & 0x7FFFFFFFu;
-  if (a == 0) return sign;
-  uint32_t sig;
-  int ex;                                 // |x| = sig * 2^ex
-  if ((a >> 23) != 0) { sig = (a & 0x7FFFFFu) | 0x800000u; ex = static_cast<int>(a >> 23) - 150; }
-  else { sig = a; ex = -149; }
-  const int t = ex + 127 - sb;            // scaled value = sig * 2^t
-  const int p = (31 - __clz(sig)) + t;    // floor(log2(scaled value))
-  int q = p - 3;                          // quantum exponent: 3 mantissa bits ...
-  if (q < -9) q = -9;                     // ... down to the subnormal step 2^-9
-  const int sh = q - t;                   // >= 0 for every finite input and sb >= 1
-  uint32_t n;
-  if (sh >= 25) {
-    n = 0;                                // below half the quantum
-  } else if (sh == 0) {
-    n = sig;
-  } else {
-    n = sig >> sh;
-    const uint32_t rem = sig & ((1u << sh) - 1u);
-    const uint32_t half = 1u << (sh - 1);
-    if (rem > half || (rem == half && (n & 1u))) ++n;
-  }
-  if (n == 0) return sign;
-  if (n >= 16) { n >>= 1; ++q; }          // rounding carried into the next binade
-  if (n < 8) return sign | n;             // subnormal (q == -9)
-  const int e = q + 10;                   // value = (n/8) 2^(q+3) = (1 + m/8) 2^(e-7)
-  const uint32_t m = n - 8;
-  if (e > 15 || (e == 15 && m == 7)) return sign | 0x7Eu;   // saturate to 448
-  return sign | (static_cast<uint32_t>(e) << 3) | m;
+// Four E4M3 codes (little-endian in a dword) of v * 2^(127 - sb).  For a
+// finite block max sb <= 246, so 2^(127 - sb) is a normal f32.
+__device__ __forceinline__ uint32_t e4m3x4(v4f v, uint32_t sb) {
+  const float f = __uint_as_float((254u - sb) << 23);
+  float y[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) y[i] = __builtin_amdgcn_fmed3f(v[i] * f, -448.0f, 448.0f);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w, true);
+  return static_cast<uint32_t>(w);
 }
 
 __global__ __launch_bounds__(256) void mx_quantize_kernel(const float *__restrict__ X, uint8_t *__restrict__ Q,
@@ -91,9 +77,7 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(const float *__restric
       m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 2)));
       m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 4)));
       const uint32_t sb = scale_byte(m);
-      uint32_t word = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) word |= e4m3_code(v[i], static_cast<int>(sb)) << (8 * i);
+      const uint32_t word = e4m3x4(v, sb);
       if (live) {
         __builtin_nontemporal_store(word, reinterpret_cast<uint32_t *>(Q + i0));
         if ((lane & 7) == 0) S[i0 >> 5] = static_cast<uint8_t>(sb);
@@ -102,8 +86,69 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(const float *__restric
   }
 }
 
+constexpr int QT_TOK = 128;                // tokens per transposed tile
+constexpr int QT_FEAT = 64;                // features per transposed tile
+constexpr int QT_PITCH = QT_TOK + 4;       // floats per LDS feature row
+
+__global__ __launch_bounds__(256) void mx_quantize_t_kernel(const float *__restrict__ X, uint8_t *__restrict__ Q,
+                                                            uint8_t *__restrict__ S, int R, int L, int tiles_f) {
+  __shared__ __attribute__((aligned(16))) float tile[QT_FEAT * QT_PITCH];
+  const int tid = threadIdx.x;
+  const int bt = blockIdx.x / tiles_f, bf = blockIdx.x - bt * tiles_f;
+  const int tok0 = bt * QT_TOK, f0 = bf * QT_FEAT;
+  // 128 token rows of 64 features: 16 threads per row, 16 rows per pass
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int idx = tid + 256 * i;
+    const int tok = idx >> 4, fq = idx & 15;
+    const int gt = tok0 + tok, gf = f0 + 4 * fq;
+    v4f v = {0.f, 0.f, 0.f, 0.f};
+    if (gt < R && gf < L)
+      v = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(X + static_cast<size_t>(gt) * L + gf));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tile[(4 * fq + j) * QT_PITCH + tok] = v[j];
+  }
+  __syncthreads();
+  const int feat = tid >> 2, blk = tid & 3;
+  const int gf = f0 + feat, gt = tok0 + 32 * blk;
+  if (gf >= L || gt >= R) return;
+  const v4f *src = reinterpret_cast<const v4f *>(tile + feat * QT_PITCH + 32 * blk);
+  v4f v[8];
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[i] = src[i];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m = max(m, __float_as_uint(v[i][j]) & 0x7FFFFFFFu);
+  }
+  const uint32_t sb = scale_byte(m);
+  v4u lo, hi;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    lo[i] = e4m3x4(v[i], sb);
+    hi[i] = e4m3x4(v[4 + i], sb);
+  }
+  uint8_t *dst = Q + static_cast<size_t>(gf) * R + gt;
+  __builtin_nontemporal_store(lo, reinterpret_cast<v4u *>(dst));
+  __builtin_nontemporal_store(hi, reinterpret_cast<v4u *>(dst + 16));
+  S[static_cast<size_t>(gf) * (R / 32) + gt / 32] = static_cast<uint8_t>(sb);
+}
+
 }  // namespace
 }  // namespace moe_gg
+
+extern "C" MOE_GG_API int moe_gg_mx_quantize_t(const float *X, uint8_t *Q, uint8_t *S, int R, int L,
+                                               hipStream_t stream) {
+  using namespace moe_gg;
+  if (!X || !Q || !S || R <= 0 || L <= 0 || R % 32) return MOE_GG_EINVAL;
+  if (L % 4) return MOE_GG_EUNSUPPORTED;
+  const int tiles_t = (R + QT_TOK - 1) / QT_TOK, tiles_f = (L + QT_FEAT - 1) / QT_FEAT;
+  const int64_t blocks = static_cast<int64_t>(tiles_t) * tiles_f;
+  if (blocks > 0x7FFFFFFF) return MOE_GG_EUNSUPPORTED;
+  hipLaunchKernelGGL(mx_quantize_t_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, X, Q, S, R, L,
+                     tiles_f);
+  return hipGetLastError() == hipSuccess ? MOE_GG_OK : MOE_GG_ELAUNCH;
+}
 
 extern "C" MOE_GG_API int moe_gg_mx_quantize(const float *X, uint8_t *Q, uint8_t *S, int R, int L,
                                              hipStream_t stream) {

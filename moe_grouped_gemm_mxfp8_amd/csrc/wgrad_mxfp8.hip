@@ -65,8 +65,11 @@ static_assert(128 * 512 <= STAGE_BYTES, "the epilogue stages 128 rows of 512 byt
 constexpr int STORES_PER_TILE = 16;           // 16-byte stores per lane per output tile
 constexpr int LOADS_PER_STEP = 18;            // stage loads a loading wave issues per step
 
+// One output tile: expert e, n-tile nt, k-tile kt.  The expert's tokens
+// [o0, o1) are covered by nk 128-token steps from tok0 = 128 floor(o0/128);
+// lo = o0 - tok0 and hi = o1 - tok0 bound the tokens that count.
 struct Tile {
-  int valid, e, nk, tok0, nt, kt;
+  int valid, e, nk, tok0, lo, hi, nt, kt;
 };
 
 // LDS byte offset of row r (0..255) inside an operand tile.
@@ -78,14 +81,16 @@ __device__ __forceinline__ Tile tile_info(int t, int total, int T, int tilesK, c
                                           const int32_t *__restrict__ off, int M) {
   Tile ti;
   ti.valid = t < total;
-  if (!ti.valid) { ti.e = ti.nk = ti.tok0 = ti.nt = ti.kt = 0; return ti; }
+  if (!ti.valid) { ti.e = ti.nk = ti.tok0 = ti.lo = ti.hi = ti.nt = ti.kt = 0; return ti; }
   const int rank = t / T;
   int u = t - rank * T;
   ti.e = __builtin_amdgcn_readfirstlane(s_order[rank]);
   const int o0 = clampi(off[ti.e], 0, M);
   const int o1 = clampi(off[ti.e + 1], o0, M);
-  ti.tok0 = o0;
-  ti.nk = (o1 - o0) / TT;
+  ti.tok0 = o0 / TT * TT;
+  ti.nk = o1 > o0 ? (o1 + TT - 1) / TT - o0 / TT : 0;
+  ti.lo = o0 - ti.tok0;
+  ti.hi = o1 - ti.tok0;
   // XCD-aware order: with T a multiple of 8, the tiles a workgroup on XCD x
   // gets (u = x mod 8) become a contiguous run of T/8 in the grouped order.
   if ((T & 7) == 0) u = (u & 7) * (T >> 3) + (u >> 3);
@@ -111,6 +116,27 @@ __device__ __forceinline__ uint32_t big_code_mask(uint32_t x) {
   return __builtin_amdgcn_perm(y << 8, y, 0x090B080Au);
 }
 
+// Zeroes the codes of the tokens outside [rlo, rhi) (step-relative) in a g^T
+// fragment of 64-token half h: dword i of lane group g holds tokens
+// 64h + 16g + 4i .. +3 (i < 4) and 64h + 32 + 16g + 4(i-4) .. +3 (i >= 4).  A
+// zero code makes the product zero, so the step then sums the expert's
+// tokens only.  Used on the first and last step of an expert whose bounds
+// are not multiples of 128.
+__device__ __forceinline__ uint32_t keep_bytes(int first, int end) {
+  // bytes j of a dword with first <= j < end, for first, end clamped to [0, 4]
+  const int a = clampi(first, 0, 4), b = clampi(end, 0, 4);
+  const uint32_t below_b = b >= 4 ? 0xFFFFFFFFu : ((1u << (8 * b)) - 1u);
+  const uint32_t below_a = a >= 4 ? 0xFFFFFFFFu : ((1u << (8 * a)) - 1u);
+  return b > a ? (below_b & ~below_a) : 0u;
+}
+__device__ __forceinline__ void mask_tokens(v8i &frag, int h, int g, int rlo, int rhi) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int t = 64 * h + (i < 4 ? 16 * g + 4 * i : 32 + 16 * g + 4 * (i - 4));
+    frag[i] = static_cast<int>(static_cast<uint32_t>(frag[i]) & keep_bytes(rlo - t, rhi - t));
+  }
+}
+
 // One 128-token step of a wave's 128 x 64 patch: 16 block-scaled MFMAs
 // (32 in the two-pass form).  The fragments of both 64-token halves are
 // read from LDS up front and the MFMAs of the first half are interleaved
@@ -118,7 +144,7 @@ __device__ __forceinline__ uint32_t big_code_mask(uint32_t x) {
 template <bool SPLIT>
 __device__ __forceinline__ void compute_step(const uint8_t *st, v16f (&acc)[4][2], const uint32_t (&xrow)[4],
                                              const uint32_t (&grow)[2], const uint32_t (&chunk_off)[2][2],
-                                             int wk, int wn, int l32, int g) {
+                                             int wk, int wn, int l32, int g, int rlo, int rhi) {
   uint32_t sx[4], sg[2];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
@@ -148,6 +174,13 @@ __device__ __forceinline__ void compute_step(const uint8_t *st, v16f (&acc)[4][2
   for (int a = 0; a < 4; ++a) x[a] = frag(xrow[a], 0);
 #pragma unroll
   for (int b = 0; b < 2; ++b) g1[b] = frag(grow[b], 1);
+  if (rlo > 0 || rhi < TT) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      mask_tokens(g0[b], 0, g, rlo, rhi);
+      mask_tokens(g1[b], 1, g, rlo, rhi);
+    }
+  }
   if constexpr (SPLIT) {
     // two passes: the g^T codes of magnitude >= 128, then the rest, so that no
     // 8-token run of the MFMA mixes a block's largest codes with its small ones.
@@ -228,7 +261,7 @@ __global__ __launch_bounds__(NTHREAD, 1) void wgrad_mxfp8_kernel(
     for (int e = tid; e < E; e += NTHREAD) {
       const int o0 = clampi(off[e], 0, M);
       const int o1 = clampi(off[e + 1], o0, M);
-      s_cnt[e] = (o1 - o0) / TT;
+      s_cnt[e] = o1 > o0 ? (o1 + TT - 1) / TT - o0 / TT : 0;
     }
     __syncthreads();
     for (int e = tid; e < E; e += NTHREAD) {
@@ -361,7 +394,7 @@ __global__ __launch_bounds__(NTHREAD, 1) void wgrad_mxfp8_kernel(
       }
 
       const uint8_t *st = smem + buf * STAGE_BYTES;
-      compute_step<SPLIT>(st, acc, xrow, grow, chunk_off, wk, wn, l32, g);
+      compute_step<SPLIT>(st, acc, xrow, grow, chunk_off, wk, wn, l32, g, cur.lo - s * TT, cur.hi - s * TT);
       buf ^= 1;
     }
 

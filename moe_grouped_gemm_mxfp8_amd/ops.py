@@ -5,7 +5,7 @@ import torch
 
 from ._lib import call
 
-__all__ = ["wgrad_mxfp8", "dgrad_f32", "mx_quantize", "row_experts"]
+__all__ = ["wgrad_mxfp8", "dgrad_f32", "mx_quantize", "mx_quantize_t", "row_experts"]
 
 
 def _stream() -> int:
@@ -86,6 +86,23 @@ def mx_quantize(x, q=None, s=None):
         s = torch.empty((R, max(L // 32, 1)), dtype=torch.uint8, device=x.device)
     _dev(q, "q", _U8); _dev(s, "s", _U8)
     call("moe_gg_mx_quantize", x.data_ptr(), q.data_ptr(), s.data_ptr(), R, L, _stream())
+    return q, s
+
+
+def mx_quantize_t(x, q=None, s=None):
+    """MX-quantise the transpose of f32 x[R, L] along R: (codes uint8 [L, R], scales uint8 [L, R/32])."""
+    _dev(x, "x", (torch.float32,))
+    if x.dim() != 2:
+        raise ValueError("x must be [R, L]")
+    R, L = x.shape
+    if q is None:
+        q = torch.empty((L, R), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty((L, max(R // 32, 1)), dtype=torch.uint8, device=x.device)
+    _dev(q, "q", _U8); _dev(s, "s", _U8)
+    if q.shape != (L, R) or s.shape != (L, max(R // 32, 1)):
+        raise ValueError("q must be [L, R] and s [L, R/32]")
+    call("moe_gg_mx_quantize_t", x.data_ptr(), q.data_ptr(), s.data_ptr(), R, L, _stream())
     return q, s
 
 

@@ -46,8 +46,10 @@ def wgrad_one_pass(ca, sa, cb, sb, off):
     """grad_w [E*N, K] as one hardware pass computes it from MX codes and scales.
 
     ca/sa: g^T codes [N, M] and scales [N, M/32]; cb/sb: x^T codes [K, M] and
-    scales [K, M/32].  Runs start at multiples of 8 of the token index
-    (expert offsets are multiples of 128, so runs never straddle experts).
+    scales [K, M/32].  Runs start at multiples of 8 of the absolute token
+    index.  An expert whose bounds are not multiples of 32 shares its edge
+    blocks with its neighbours: there the other tokens' g^T codes count as
+    zero, so their products take no part in the run.
     """
     ca, cb = np.asarray(ca), np.asarray(cb)
     N, M = ca.shape
@@ -60,9 +62,12 @@ def wgrad_one_pass(ca, sa, cb, sb, off):
         o0, o1 = int(off[e]), int(off[e + 1])
         if o1 == o0:
             continue
-        blocks = np.arange(o0 // 32, o1 // 32)
+        t0, t1 = o0 // 32 * 32, -(-o1 // 32) * 32
+        blocks = np.arange(t0 // 32, t1 // 32)
+        inside = (np.arange(t0, t1) >= o0) & (np.arange(t0, t1) < o1)
         for n in range(N):
-            rs = run_sums(va[n, o0:o1][None, :] * vb[:, o0:o1], ea[n, o0:o1][None, :] + eb[:, o0:o1])
+            pa = np.where(inside, va[n, t0:t1], 0.0)
+            rs = run_sums(pa[None, :] * vb[:, t0:t1], ea[n, t0:t1][None, :] + eb[:, t0:t1])
             bs = rs.reshape(K, -1, 4).sum(axis=-1)                       # [K, blocks]
             scale = np.exp2(sa[n, blocks].astype(np.int64)[None, :] + sb[:, blocks].astype(np.int64) - 254)
             out[e, n] = (bs * scale).sum(axis=-1)

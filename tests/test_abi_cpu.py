@@ -28,7 +28,7 @@ def lib():
 def test_header_declares_the_entry_points():
     names = _declared()
     for want in ("moe_gg_wgrad_mxfp8", "moe_gg_wgrad_mxfp8_fast", "moe_gg_dgrad_f32", "moe_gg_mx_quantize",
-                 "moe_gg_row_experts", "moe_gg_status_string"):
+                 "moe_gg_mx_quantize_t", "moe_gg_row_experts", "moe_gg_status_string"):
         assert want in names
 
 
@@ -77,6 +77,10 @@ def test_host_validation_dgrad_quantize_rows(lib):
     assert lib.moe_gg_mx_quantize(p, p, None, 4, 64, None) == -1
     assert lib.moe_gg_mx_quantize(p, p, p, 4, 48, None) == -1
     assert lib.moe_gg_mx_quantize(p, p, p, 0, 64, None) == -1
+    assert lib.moe_gg_mx_quantize_t(p, p, None, 64, 8, None) == -1
+    assert lib.moe_gg_mx_quantize_t(p, p, p, 48, 8, None) == -1      # R % 32
+    assert lib.moe_gg_mx_quantize_t(p, p, p, 64, 0, None) == -1
+    assert lib.moe_gg_mx_quantize_t(p, p, p, 64, 6, None) == -2      # L % 4
     assert lib.moe_gg_row_experts(p, 0, 10, p, None) == -1
     assert lib.moe_gg_row_experts(None, 2, 10, p, None) == -1
 
@@ -86,5 +90,7 @@ def test_python_binding_refuses_cpu_tensors():
     import moe_grouped_gemm_mxfp8_amd as mg
     with pytest.raises(ValueError):
         mg.mx_quantize(torch.zeros(4, 64))
+    with pytest.raises(ValueError):
+        mg.mx_quantize_t(torch.zeros(64, 4))
     with pytest.raises(ValueError):
         mg.dgrad_f32(torch.zeros(4, 4), torch.zeros(1, 4, 4), torch.zeros(2, dtype=torch.int32))

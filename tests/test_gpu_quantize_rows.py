@@ -66,6 +66,43 @@ def test_quantize_workload_inputs(idx):
         assert np.array_equal(host(q), want_q)
 
 
+@pytest.mark.parametrize("case", ["edge", "tile", "ragged", "tall"])
+def test_quantize_transposed_bit_exact(case):
+    """moe_gg_mx_quantize_t(x) equals the oracle's quantisation of x^T, code for code."""
+    torch, mg = require_gpu()
+    rng = np.random.default_rng({"edge": 11, "tile": 12, "ragged": 13, "tall": 14}[case])
+    if case == "edge":
+        x = np.ascontiguousarray(_edge_input().T)            # [128 tokens, 12 features]
+    elif case == "tile":
+        x = rng.standard_normal((256, 128)).astype(np.float32)
+    elif case == "ragged":                                    # partial tiles in both directions
+        x = (rng.standard_normal((160, 100)) * np.exp2(rng.integers(-40, 40, (1, 100)))).astype(np.float32)
+    else:
+        x = rng.standard_normal((4096 + 32, 36)).astype(np.float32)
+        x[rng.random(x.shape) < 0.01] *= 64
+    say("quantize_t", case, x.shape)
+    q, s = mg.mx_quantize_t(dev(torch, x))
+    torch.cuda.synchronize()
+    want_q, want_s = oracle.mx_quantize(np.ascontiguousarray(x.T))
+    assert np.array_equal(host(s), want_s)
+    got_q = host(q)
+    bad = np.argwhere(got_q != want_q)
+    assert bad.size == 0, (bad[:5], got_q[tuple(bad[0])], want_q[tuple(bad[0])])
+
+
+def test_quantize_transposed_workload_operand():
+    """g [M, N] of the 8192^3 workload -> g^T codes, as the weight gradient's A operand."""
+    torch, mg = require_gpu()
+    inp = wl.make_wgrad_inputs(4)
+    g = np.ascontiguousarray(inp["gT"].T)                     # [M = 8192 tokens, N = 8192]
+    say("quantize_t workload 4 g", g.shape)
+    q, s = mg.mx_quantize_t(dev(torch, g))
+    torch.cuda.synchronize()
+    want_q, want_s = oracle.mx_quantize(inp["gT"])
+    assert np.array_equal(host(s), want_s)
+    assert np.array_equal(host(q), want_q)
+
+
 OFFSETS = [
     [0, 256],
     [0, 0, 0, 100, 100, 256],

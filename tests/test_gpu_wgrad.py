@@ -38,6 +38,11 @@ CASES = {
     "all_empty_but_one": (256, 256, [0, 0, 0, 128, 0]),
     "many_experts": (256, 256, [128] * 3 + [0] * 2 + [256] * 2 + [128] * 5),
     "deep_k": (256, 256, [1024, 128]),
+    # expert bounds that are not multiples of 128 (nor of 32): masked edge steps
+    "unaligned": (256, 256, [100, 0, 37, 300, 75]),
+    "unaligned_tiny": (256, 512, [1, 126, 1, 0, 128]),
+    "unaligned_many": (512, 256, [33, 95, 200, 56, 0, 128, 40, 88]),
+    "unaligned_shared_step": (256, 256, [60, 4, 64, 0, 128]),
 }
 
 
@@ -149,6 +154,30 @@ def test_wgrad_full_size_sampled(idx):
     assert oracle.wgrad_excess(out, ref, ref_rms=ref_rms) <= 0
 
 
+def test_wgrad_full_size_unaligned_offsets():
+    """The 8192^3 workload with expert bounds moved off the 128 (and 32) grid."""
+    torch, mg = require_gpu()
+    w = wl.WORKLOADS[4]
+    inp = wl.make_wgrad_inputs(4)
+    counts = np.array([3200 - 37, 1536 + 42, 1024 - 5, 640, 512, 512 - 7, 384 + 7, 384])
+    off = wl.offsets_from_counts(counts)
+    assert int(off[-1]) == w.M
+    ca, sa, cb, sb = _mx_inputs(inp["gT"], inp["xT"])
+    del inp
+    say("wgrad workload 4 full size, unaligned offsets", list(off))
+    got = mg.wgrad_mxfp8(dev(torch, ca), dev(torch, cb), dev(torch, sa), dev(torch, sb), dev(torch, off))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(204)
+    refs, outs = [], []
+    for e in range(w.E):
+        rows = sample_rows(rng, w.N, 8, must=(0, 255, 256, w.N - 1))
+        refs.append(oracle.wgrad_rows(ca, sa, cb, sb, off, e, rows))
+        outs.append(host(got[e * w.N:(e + 1) * w.N][rows]).astype(np.float64))
+    ref = np.concatenate(refs)
+    out = np.concatenate(outs)
+    assert oracle.wgrad_excess(out, ref, ref_rms=np.sqrt(np.mean(ref * ref))) <= 0
+
+
 # ---- the single-pass entry point (moe_gg_wgrad_mxfp8_fast) -------------------
 
 def _run_fast(torch, mg, ca, sa, cb, sb, off):
@@ -158,7 +187,8 @@ def _run_fast(torch, mg, ca, sa, cb, sb, off):
     return host(out).astype(np.float64)
 
 
-@pytest.mark.parametrize("name", ["two_tiles_each", "empty_middle", "many_experts", "deep_k"])
+@pytest.mark.parametrize("name", ["two_tiles_each", "empty_middle", "many_experts", "deep_k", "unaligned",
+                                  "unaligned_many"])
 def test_wgrad_fast_follows_hardware_rounding(name):
     """With 64x outliers the single pass follows the measured run-of-8 rounding model."""
     import hw_mfma_model as hw
