@@ -10,7 +10,8 @@ matmul per expert segment.
 
 Modules:
   mx         E4M3 / E8M0 codec and the MX quantiser (32-element blocks).
-  grouped    expert lookup, grouped wgrad (MX inputs) and grouped dgrad (f32).
+  grouped    expert lookup, grouped wgrad (MX inputs), grouped dgrad (f32) and
+             the expert-grouped MX GEMM (forward / MXFP8 data gradient).
   tolerance  the acceptance bounds used to compare a result with the oracle.
 
 Every function is pinned by ``tests/test_oracle_*.py`` against closed forms,
@@ -19,14 +20,14 @@ none is "parity unpinned".
 """
 from .mx import (E4M3_MAX, E4M3_VALUES, MX_BLOCK, e4m3_value, e8m0_value,
                  mx_dequantize, mx_quantize, mx_scale_bytes, round_to_e4m3)
-from .grouped import (check_offsets, dgrad, dgrad_rows, row_experts, wgrad,
-                      wgrad_from_dequantized, wgrad_rows)
+from .grouped import (check_offsets, dgrad, dgrad_rows, grouped_gemm, grouped_gemm_rows,
+                      row_experts, wgrad, wgrad_from_dequantized, wgrad_rows)
 from .tolerance import dgrad_bound, dgrad_ok, rms, wgrad_excess, wgrad_ok
 
 __all__ = [
     "E4M3_MAX", "E4M3_VALUES", "MX_BLOCK", "e4m3_value", "e8m0_value",
     "mx_dequantize", "mx_quantize", "mx_scale_bytes", "round_to_e4m3",
-    "check_offsets", "dgrad", "dgrad_rows", "row_experts", "wgrad",
+    "check_offsets", "dgrad", "dgrad_rows", "grouped_gemm", "grouped_gemm_rows", "row_experts", "wgrad",
     "wgrad_from_dequantized", "wgrad_rows",
     "dgrad_bound", "dgrad_ok", "rms", "wgrad_excess", "wgrad_ok",
 ]

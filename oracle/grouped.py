@@ -20,6 +20,13 @@ off[e] <= m < off[e+1] (half-open, so an empty expert owns nothing).
   span several experts, which is the plain definition):
       dx[r, k] = sum_n g[r, n] * W[e(r), n, k]
   in fp64 from the f32 inputs, one matmul per expert segment.
+* Expert-grouped MX GEMM (the MoE forward y = x W_e^T and, with the weights
+  transposed, an MXFP8 data gradient): token rows bucketed by ``off`` as
+  above, both operands MX-quantised along the contraction (the vLLM page's
+  mfma_f8f8: fp8 weights with one E8M0 scale per 32 along k, times fp8
+  activations):
+      C[r, j] = sum_c A[r, c] * B[e(r), j, c]
+  with A and B dequantised, one fp64 matmul per expert segment.
 """
 from __future__ import annotations
 
@@ -28,7 +35,8 @@ import numpy as np
 from .mx import mx_dequantize
 
 __all__ = ["check_offsets", "row_experts", "wgrad", "wgrad_rows",
-           "wgrad_from_dequantized", "dgrad", "dgrad_rows"]
+           "wgrad_from_dequantized", "dgrad", "dgrad_rows",
+           "grouped_gemm", "grouped_gemm_rows"]
 
 
 def check_offsets(off, M: int, align: int = 1) -> np.ndarray:
@@ -136,4 +144,42 @@ def dgrad_rows(g, W, off, rows) -> np.ndarray:
     out = np.empty((rows.size, W.shape[2]), dtype=np.float64)
     for i, (r, e) in enumerate(zip(rows, experts)):
         out[i] = g[r].astype(np.float64) @ W[e].astype(np.float64)
+    return out
+
+
+def grouped_gemm(codes_a, scales_a, codes_b, scales_b, off) -> np.ndarray:
+    """Expert-grouped MX GEMM, fp64 [M, N].
+
+    codes_a/scales_a: A as E4M3 [M, K] and E8M0 [M, K/32] (token rows);
+    codes_b/scales_b: B as E4M3 [E, N, K] and E8M0 [E, N, K/32].
+    C[r] = deq(A)[r] @ deq(B[e(r)]).T for the expert e(r) that owns row r.
+    """
+    codes_a = np.asarray(codes_a)
+    codes_b = np.asarray(codes_b)
+    M, K = codes_a.shape
+    E, N, Kb = codes_b.shape
+    if Kb != K:
+        raise ValueError("A and B must share the contraction axis")
+    off = check_offsets(off, M)
+    if off.size != E + 1:
+        raise ValueError("offsets must have E+1 entries")
+    a = mx_dequantize(codes_a, scales_a)
+    out = np.zeros((M, N), dtype=np.float64)
+    for e in range(E):
+        o0, o1 = int(off[e]), int(off[e + 1])
+        if o1 > o0:
+            out[o0:o1] = a[o0:o1] @ mx_dequantize(codes_b[e], scales_b[e]).T
+    return out
+
+
+def grouped_gemm_rows(codes_a, scales_a, codes_b, scales_b, off, rows) -> np.ndarray:
+    """Rows ``rows`` of the grouped MX GEMM, fp64 [len(rows), N]; each row uses its own expert."""
+    M = np.asarray(codes_a).shape[0]
+    rows = np.asarray(rows, dtype=np.int64)
+    experts = row_experts(off, M)[rows]
+    a = mx_dequantize(np.asarray(codes_a)[rows], np.asarray(scales_a)[rows])
+    out = np.empty((rows.size, np.asarray(codes_b).shape[1]), dtype=np.float64)
+    for e in np.unique(experts):
+        sel = experts == e
+        out[sel] = a[sel] @ mx_dequantize(codes_b[e], scales_b[e]).T
     return out

@@ -231,3 +231,88 @@ def test_tolerances():
     assert not oracle.wgrad_ok(bad, ref)
     assert oracle.dgrad_ok(ref * (1 + 1e-6), ref, 1024)
     assert not oracle.dgrad_ok(ref + 1e-3 * np.abs(ref).max(), ref, 1024)
+
+
+# ---- expert-grouped MX GEMM ------------------------------------------------
+
+def _brute_grouped(ca, sa, cb, sb, off):
+    """C[m][j] = sum over c of a[m,c] * b[e(m)][j,c], exactly; e(m) by a linear scan."""
+    M, K = ca.shape
+    E, N, _ = cb.shape
+    out = np.zeros((M, N), dtype=np.float64)
+    for m in range(M):
+        e = max(i for i in range(E) if off[i] <= m)      # last expert starting at or before m
+        while off[e + 1] <= m:                           # (never taken for valid offsets)
+            e += 1
+        for j in range(N):
+            acc = Fraction(0)
+            for c in range(K):
+                acc += _exact(ca[m, c], sa[m, c // 32]) * _exact(cb[e, j, c], sb[e, j, c // 32])
+            out[m, j] = float(acc)
+    return out
+
+
+@pytest.mark.parametrize("off", [[0, 3, 3, 7], [0, 0, 5, 7], [0, 7, 7, 7], [0, 1, 2, 7]])
+def test_grouped_gemm_brute_force_exact(off):
+    rng = np.random.default_rng(sum(off) + 50)
+    M, K, N, E = 7, 64, 3, 3
+    ca, sa = _rand_mx(rng, M, K)
+    cb, sb = _rand_mx(rng, E * N, K)
+    cb, sb = cb.reshape(E, N, K), sb.reshape(E, N, K // 32)
+    got = oracle.grouped_gemm(ca, sa, cb, sb, off)
+    want = _brute_grouped(ca, sa, cb, sb, off)
+    # exact products; the oracle's fp64 sums round, the brute force rounds once
+    assert np.max(np.abs(got - want)) <= 1e-13 * (np.abs(want).max() + 1e-300)
+
+
+def test_grouped_gemm_is_the_data_gradient_of_the_dequantised_weights():
+    """With B[e] = W_e^T the grouped GEMM is the grouped data gradient g @ W_e."""
+    rng = np.random.default_rng(61)
+    M, K, N, E = 96, 128, 40, 4
+    off = [0, 10, 10, 70, 96]
+    ca, sa = _rand_mx(rng, M, K)
+    cb, sb = _rand_mx(rng, E * N, K)
+    cb, sb = cb.reshape(E, N, K), sb.reshape(E, N, K // 32)
+    g = mx.mx_dequantize(ca, sa)                                        # [M, K]
+    W = np.stack([mx.mx_dequantize(cb[e], sb[e]).T for e in range(E)])  # [E, K, N]
+    np.testing.assert_allclose(oracle.grouped_gemm(ca, sa, cb, sb, off), oracle.dgrad(g, W, off),
+                               rtol=1e-12, atol=1e-12)
+
+
+def test_grouped_gemm_all_ones_counts_the_contraction():
+    M, K, N, E = 64, 96, 8, 2
+    ca = np.full((M, K), 0x38, np.uint8)                 # 1.0
+    sa = np.full((M, K // 32), 127, np.uint8)
+    cb = np.full((E, N, K), 0x38, np.uint8)
+    sb = np.full((E, N, K // 32), 127, np.uint8)
+    assert np.array_equal(oracle.grouped_gemm(ca, sa, cb, sb, [0, 20, 64]), np.full((M, N), float(K)))
+
+
+def test_grouped_gemm_scale_only_probe():
+    """Codes 1.0 and varied scales: each block adds 32 * 2^(sa + sb - 254)."""
+    M, K, N, E = 4, 128, 2, 2
+    ca = np.full((M, K), 0x38, np.uint8)
+    cb = np.full((E, N, K), 0x38, np.uint8)
+    sa = np.array([[127, 128, 126, 130]] * M, np.uint8)
+    sb = np.zeros((E, N, K // 32), np.uint8)
+    sb[0] = [[127, 127, 127, 127], [120, 121, 122, 123]]
+    sb[1] = [[130, 127, 127, 127], [127, 127, 127, 100]]
+    off = [0, 1, 4]
+    got = oracle.grouped_gemm(ca, sa, cb, sb, off)
+    for m in range(M):
+        e = 0 if m < 1 else 1
+        for j in range(N):
+            want = sum(32 * 2.0 ** (int(sa[m, b]) + int(sb[e, j, b]) - 254) for b in range(K // 32))
+            assert got[m, j] == want
+
+
+def test_grouped_gemm_rows_match_the_whole_product():
+    rng = np.random.default_rng(62)
+    M, K, N, E = 80, 64, 24, 3
+    off = [0, 33, 33, 80]
+    ca, sa = _rand_mx(rng, M, K)
+    cb, sb = _rand_mx(rng, E * N, K)
+    cb, sb = cb.reshape(E, N, K), sb.reshape(E, N, K // 32)
+    whole = oracle.grouped_gemm(ca, sa, cb, sb, off)
+    rows = [0, 32, 33, 34, 79]
+    assert np.array_equal(oracle.grouped_gemm_rows(ca, sa, cb, sb, off, rows), whole[rows])
