@@ -38,13 +38,14 @@ PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 
 KERNEL_SOURCES = {
-    "wgrad": ["wgrad_mxfp8.hip", "common.hpp"],
+    "wgrad": ["wgrad_mxfp8.hip", "mx_gemm_core.hpp", "common.hpp"],
     "dgrad": ["dgrad_f32.hip", "common.hpp"],
     "quantize": ["mx_quantize.hip", "common.hpp"],
     "quantize_t": ["mx_quantize.hip", "common.hpp"],
+    "grouped": ["grouped_mxfp8.hip", "mx_gemm_core.hpp", "common.hpp"],
 }
 KERNEL_NAMES = {"wgrad": "wgrad_mxfp8_kernel", "dgrad": "dgrad_f32_kernel", "quantize": "mx_quantize_kernel",
-                "quantize_t": "mx_quantize_t_kernel"}
+                "quantize_t": "mx_quantize_t_kernel", "grouped": "grouped_mxfp8_kernel"}
 
 
 def source_digest(pass_name: str) -> str:
@@ -206,6 +207,53 @@ def bench_dgrad(torch, mg, idx, steps, warmup, cpu_baseline):
     return line
 
 
+def bench_grouped(torch, mg, idx, steps, warmup, cpu_baseline, fast=False):
+    """The expert-grouped MXFP8 GEMM as an MXFP8 data gradient of a dgrad workload:
+    dx = g W_e with A = MX(g) along N and B[e] = MX(W_e^T) along N (both quantised on the GPU)."""
+    inp = wl.make_dgrad_inputs(idx)
+    d = torch.device("cuda:0")
+    g = torch.from_numpy(inp["g"]).to(d)
+    W = torch.from_numpy(inp["W"]).to(d)
+    off = torch.from_numpy(inp["off"]).to(d)
+    M, N = g.shape
+    E, _, K = W.shape
+    qa, sa = mg.mx_quantize(g)                                   # [M, N] along N
+    qb = torch.empty((E, K, N), dtype=torch.uint8, device=d)
+    sb = torch.empty((E, K, N // 32), dtype=torch.uint8, device=d)
+    for e in range(E):
+        mg.mx_quantize_t(W[e], qb[e], sb[e])                     # W_e [N, K] -> [K, N] along N
+    torch.cuda.synchronize()
+    del W
+    out = torch.empty((M, K), dtype=torch.bfloat16, device=d)
+    ms = time_steps(torch, lambda: mg.grouped_mxfp8(qa, qb, sa, sb, off, out=out, fast=fast), steps, warmup)
+    flop = 2.0 * M * N * K
+    tf = flop / (ms * 1e-3) / 1e12
+    nbytes = M * N + M * N // 32 + 2 * M * K + sum(
+        (N * K + N * K // 32) for e in range(E) if inp["off"][e + 1] > inp["off"][e])
+    line = {"metric": f"TFLOP/s, expert-grouped MXFP8 GEMM as the data gradient of workload {idx} (1 GPU)",
+            "value": round(tf, 2), "unit": "TFLOP/s", "pct_of_fp8_peak": round(100 * tf / PEAK_FP8_TFLOPS, 2),
+            "ms_per_step": round(ms, 4), "dtype": "fp8e4m3*fp8e4m3->f32 acc, bf16 out",
+            "mode": "single block-scaled MFMA pass" if fast else "two block-scaled MFMA passes (A codes >= 128 / the rest)",
+            "config": {"workload": wl.WORKLOADS[idx].name, "E": E, "M": M, "contraction": N, "N_out": K},
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_FP8_TFLOPS, 4), "traffic": None,
+                         "algorithmic_bytes": int(nbytes), "algorithmic_flop": flop}}
+    if cpu_baseline:
+        import oracle
+        qa_h, sa_h = qa.cpu().numpy(), sa.cpu().numpy()
+        rows = int(inp["off"][E // 8])                            # the tokens of the first E/8 experts
+        sub_off = inp["off"][: E // 8 + 1]
+        qb_h, sb_h = qb[: E // 8].cpu().numpy(), sb[: E // 8].cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.grouped_gemm(qa_h[:rows], sa_h[:rows], qb_h, sb_h, sub_off)
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": round(2.0 * rows * N * K / dt / 1e12, 4), "unit": "TFLOP/s",
+                                "cores": blas_threads(), "kind": "oracle", "seconds": round(dt, 2),
+                                "cpu": cpu_info(),
+                                "sample": f"the {rows} token rows of experts 0..{E // 8 - 1} (oracle.grouped_gemm, fp64)"}
+    return line
+
+
 def bench_quantize(torch, mg, idx, steps, warmup, cpu_baseline):
     inp = wl.make_wgrad_inputs(idx)
     d = torch.device("cuda:0")
@@ -282,7 +330,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--pass", dest="pass_name", choices=["wgrad", "dgrad", "quantize", "quantize_t", "copy"], default="wgrad")
+    ap.add_argument("--pass", dest="pass_name", choices=["wgrad", "grouped", "dgrad", "quantize", "quantize_t", "copy"], default="wgrad")
     ap.add_argument("--workload", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fast", action="store_true", help="wgrad: the single-pass entry point")
@@ -299,10 +347,11 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
 
-    idx = args.workload or {"wgrad": 4, "dgrad": 5, "quantize": 4, "quantize_t": 4, "copy": 0}[args.pass_name]
-    fn = {"wgrad": bench_wgrad, "dgrad": bench_dgrad, "quantize": bench_quantize, "quantize_t": bench_quantize_t,
-          "copy": bench_copy}[args.pass_name]
-    kw = {"fast": True} if (args.fast and args.pass_name == "wgrad") else {}
+    idx = args.workload or {"wgrad": 4, "grouped": 5, "dgrad": 5, "quantize": 4, "quantize_t": 4,
+                            "copy": 0}[args.pass_name]
+    fn = {"wgrad": bench_wgrad, "grouped": bench_grouped, "dgrad": bench_dgrad, "quantize": bench_quantize,
+          "quantize_t": bench_quantize_t, "copy": bench_copy}[args.pass_name]
+    kw = {"fast": True} if (args.fast and args.pass_name in ("wgrad", "grouped")) else {}
     line = fn(torch, mg, idx, args.steps, args.warmup, not args.no_cpu_baseline, **kw)
     line.update({"n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
                  "higher_is_better": True, "scaling": "weak", "vs_baseline": None,

@@ -126,6 +126,51 @@ MOE_GG_API int moe_gg_dgrad_f32(const float *A, const float *B, float *C,
                                 hipStream_t stream);
 
 /*
+ * Expert-grouped MXFP8 GEMM (the MoE forward, and with transposed weights an
+ * MXFP8 data gradient).
+ *
+ * Source: the tinygrad page's expert_off bucketing of token rows and the
+ * Slang page's expert_for_row (each row uses its own expert's weights); the
+ * vLLM page's mfma_f8f8 (fp8 weights with one E8M0 scale per 32 along the
+ * contraction, times fp8 activations, on the block-scaled MFMA).
+ *
+ *   A        E4M3 bytes [M][K]      (token rows, contraction contiguous)
+ *   B        E4M3 bytes [E][N][K]   (expert e's weights, contraction contiguous)
+ *   C        bf16 bits  [M][N], every element written
+ *   scale_A  E8M0 [M][K/32]; scale_B  E8M0 [E][N][K/32]
+ *   expert_off int32 [E+1]: off[0] = 0, nondecreasing, off[E] = M (any
+ *            alignment; clamped to [0, M] on the device)
+ *
+ *   C[m][j] = bf16_rne( sum over c of deq(A)[m][c] deq(B[e(m)])[j][c] ),
+ *   accumulated in f32, e(m) the expert with off[e] <= m < off[e+1]; rows of
+ *   no expert (malformed offsets) are +0.0.
+ *
+ * Forward y = x W_e^T: A = MX(x) along K, B[e] = MX(W_e) along K.
+ * Data gradient dx = g W_e with W_e [N][K]: A = MX(g) along N (this call's K
+ * is N), B[e] = moe_gg_mx_quantize_t(W_e) ([K][N] along N).
+ *
+ * Shapes: M, N, K, E >= 1 and K % 32 == 0 (EINVAL otherwise); N % 256 == 0
+ * and K % 128 == 0 (EUNSUPPORTED otherwise).  Accuracy as for the weight
+ * gradient: this entry point splits A's codes into two MFMA passes (codes of
+ * magnitude >= 128 and the rest), which keeps the result within
+ * 2^-7 |ref| + 2^-12 rms(ref) of the exact sum also with 64x outliers in A.
+ */
+MOE_GG_API int moe_gg_grouped_mxfp8(const uint8_t *A, const uint8_t *B, uint16_t *C,
+                                    const uint8_t *scale_A, const uint8_t *scale_B,
+                                    const int32_t *expert_off, int M, int N, int K, int E,
+                                    hipStream_t stream);
+
+/*
+ * The same expert-grouped GEMM in one block-scaled MFMA pass (the hardware's
+ * own reduction; see moe_gg_wgrad_mxfp8_fast).  Same arguments and status
+ * codes.
+ */
+MOE_GG_API int moe_gg_grouped_mxfp8_fast(const uint8_t *A, const uint8_t *B, uint16_t *C,
+                                         const uint8_t *scale_A, const uint8_t *scale_B,
+                                         const int32_t *expert_off, int M, int N, int K, int E,
+                                         hipStream_t stream);
+
+/*
  * MX quantiser: f32 [R][L] -> E4M3 codes [R][L] + E8M0 scales [R][L/32],
  * blocks of 32 consecutive elements along L (aligned to the start of a row).
  *

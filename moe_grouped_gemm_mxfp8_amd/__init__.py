@@ -5,6 +5,7 @@ Python entry points (thin wrappers over the C ABI; torch supplies device
 memory and the current stream, nothing else):
 
   wgrad_mxfp8(a, b, scale_a, scale_b, expert_off, out=None, fast=False) -> bf16 [E*N, K]
+  grouped_mxfp8(a, b, scale_a, scale_b, expert_off, out=None, fast=False) -> bf16 [M, N]
   dgrad_f32(g, w, expert_off, out=None)                     -> f32 [M, K]
   mx_quantize(x, q=None, s=None)                            -> (uint8 [R, L], uint8 [R, L/32])
   mx_quantize_t(x, q=None, s=None)                          -> (uint8 [L, R], uint8 [L, R/32])
@@ -16,7 +17,7 @@ without a GPU raises.
 from __future__ import annotations
 
 from ._lib import EINVAL, ELAUNCH, EUNSUPPORTED, OK, MoeGGError, status_string
-from .ops import dgrad_f32, mx_quantize, mx_quantize_t, row_experts, wgrad_mxfp8
+from .ops import dgrad_f32, grouped_mxfp8, mx_quantize, mx_quantize_t, row_experts, wgrad_mxfp8
 
-__all__ = ["wgrad_mxfp8", "dgrad_f32", "mx_quantize", "mx_quantize_t", "row_experts", "status_string",
+__all__ = ["wgrad_mxfp8", "grouped_mxfp8", "dgrad_f32", "mx_quantize", "mx_quantize_t", "row_experts", "status_string",
            "MoeGGError", "OK", "EINVAL", "EUNSUPPORTED", "ELAUNCH"]

@@ -21,6 +21,8 @@ _I = ctypes.c_int
 SIGNATURES = {
     "moe_gg_wgrad_mxfp8": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _VP]),
     "moe_gg_wgrad_mxfp8_fast": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _VP]),
+    "moe_gg_grouped_mxfp8": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _VP]),
+    "moe_gg_grouped_mxfp8_fast": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _VP]),
     "moe_gg_dgrad_f32": (_I, [_VP, _VP, _VP, _VP, _I, _I, _I, _I, _VP]),
     "moe_gg_mx_quantize": (_I, [_VP, _VP, _VP, _I, _I, _VP]),
     "moe_gg_mx_quantize_t": (_I, [_VP, _VP, _VP, _I, _I, _VP]),

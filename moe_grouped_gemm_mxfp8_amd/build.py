@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe_gg.so")
-SOURCES = ["wgrad_mxfp8.hip", "dgrad_f32.hip", "mx_quantize.hip", "status.cpp"]
+SOURCES = ["wgrad_mxfp8.hip", "grouped_mxfp8.hip", "dgrad_f32.hip", "mx_quantize.hip", "status.cpp"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in any generated code.

@@ -5,7 +5,7 @@ import torch
 
 from ._lib import call
 
-__all__ = ["wgrad_mxfp8", "dgrad_f32", "mx_quantize", "mx_quantize_t", "row_experts"]
+__all__ = ["wgrad_mxfp8", "grouped_mxfp8", "dgrad_f32", "mx_quantize", "mx_quantize_t", "row_experts"]
 
 
 def _stream() -> int:
@@ -71,6 +71,33 @@ def dgrad_f32(g, w, expert_off, out=None):
         raise ValueError("out must be [M, K]")
     call("moe_gg_dgrad_f32", g.data_ptr(), w.data_ptr(), out.data_ptr(), expert_off.data_ptr(),
          M, N, K, E, _stream())
+    return out
+
+
+def grouped_mxfp8(a, b, scale_a, scale_b, expert_off, out=None, fast=False):
+    """Expert-grouped MXFP8 GEMM: out[m] = deq(a)[m] @ deq(b[e(m)]).T as bf16 [M, N].
+
+    a: uint8 E4M3 [M, K]; b: uint8 E4M3 [E, N, K]; scale_a [M, K/32], scale_b [E, N, K/32];
+    expert_off int32 [E+1].
+    """
+    for t, name in ((a, "a"), (b, "b"), (scale_a, "scale_a"), (scale_b, "scale_b")):
+        _dev(t, name, _U8)
+    _dev(expert_off, "expert_off", (torch.int32,))
+    if a.dim() != 2 or b.dim() != 3 or b.shape[2] != a.shape[1]:
+        raise ValueError("a must be [M, K] and b [E, N, K]")
+    M, K = a.shape
+    E, N, _ = b.shape
+    if scale_a.shape != (M, K // 32) or scale_b.shape != (E, N, K // 32):
+        raise ValueError("scale_a must be [M, K/32] and scale_b [E, N, K/32]")
+    if expert_off.numel() != E + 1:
+        raise ValueError("expert_off must have E+1 entries")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    _dev(out, "out", (torch.bfloat16,))
+    if out.shape != (M, N):
+        raise ValueError("out must be [M, N]")
+    call("moe_gg_grouped_mxfp8_fast" if fast else "moe_gg_grouped_mxfp8", a.data_ptr(), b.data_ptr(),
+         out.data_ptr(), scale_a.data_ptr(), scale_b.data_ptr(), expert_off.data_ptr(), M, N, K, E, _stream())
     return out
 
 

@@ -27,7 +27,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     names = _declared()
-    for want in ("moe_gg_wgrad_mxfp8", "moe_gg_wgrad_mxfp8_fast", "moe_gg_dgrad_f32", "moe_gg_mx_quantize",
+    for want in ("moe_gg_wgrad_mxfp8", "moe_gg_wgrad_mxfp8_fast", "moe_gg_grouped_mxfp8",
+                 "moe_gg_grouped_mxfp8_fast", "moe_gg_dgrad_f32", "moe_gg_mx_quantize",
                  "moe_gg_mx_quantize_t", "moe_gg_row_experts", "moe_gg_status_string"):
         assert want in names
 
@@ -67,6 +68,20 @@ def test_host_validation_wgrad(lib, name):
     assert f(p, p, p, p, p, p, 256, 200, 256, 2, None) == -2       # N % 256
     assert f(p, p, p, p, p, p, 256, 256, 384, 2, None) == -2       # K % 256
     assert f(p, p, p, p, p, p, 256, 256, 256, 2000, None) == -2    # E above the ranking table
+
+
+@pytest.mark.parametrize("name", ["moe_gg_grouped_mxfp8", "moe_gg_grouped_mxfp8_fast"])
+def test_host_validation_grouped(lib, name):
+    f = getattr(lib, name)
+    p = ctypes.c_void_p(16)
+    ok = (300, 256, 256, 3)                                         # M need not be a tile multiple
+    assert f(None, p, p, p, p, p, *ok, None) == -1
+    assert f(p, p, p, p, p, None, *ok, None) == -1
+    assert f(p, p, p, p, p, p, 0, 256, 256, 3, None) == -1
+    assert f(p, p, p, p, p, p, 300, 256, 256, 0, None) == -1
+    assert f(p, p, p, p, p, p, 300, 256, 48, 3, None) == -1        # K % 32
+    assert f(p, p, p, p, p, p, 300, 200, 256, 3, None) == -2       # N % 256
+    assert f(p, p, p, p, p, p, 300, 256, 160, 3, None) == -2       # K % 128
 
 
 def test_host_validation_dgrad_quantize_rows(lib):
