@@ -139,18 +139,20 @@ MOE_GG_API int moe_gg_dgrad_f32(const float *A, const float *B, float *C,
  *   C        bf16 bits  [M][N], every element written
  *   scale_A  E8M0 [M][K/32]; scale_B  E8M0 [E][N][K/32]
  *   expert_off int32 [E+1]: off[0] = 0, nondecreasing, off[E] = M (any
- *            alignment; clamped to [0, M] on the device)
+ *            alignment).  On the device each entry is clamped to [0, M] and
+ *            raised to the largest entry before it, which leaves well-formed
+ *            offsets as they are and gives any others disjoint row ranges.
  *
  *   C[m][j] = bf16_rne( sum over c of deq(A)[m][c] deq(B[e(m)])[j][c] ),
  *   accumulated in f32, e(m) the expert with off[e] <= m < off[e+1]; rows of
- *   no expert (malformed offsets) are +0.0.
+ *   no expert (off[0] > 0 or off[E] < M) are +0.0.
  *
  * Forward y = x W_e^T: A = MX(x) along K, B[e] = MX(W_e) along K.
  * Data gradient dx = g W_e with W_e [N][K]: A = MX(g) along N (this call's K
  * is N), B[e] = moe_gg_mx_quantize_t(W_e) ([K][N] along N).
  *
- * Shapes: M, N, K, E >= 1 and K % 32 == 0 (EINVAL otherwise); N % 256 == 0
- * and K % 128 == 0 (EUNSUPPORTED otherwise).  Accuracy as for the weight
+ * Shapes: M, N, K, E >= 1 and K % 32 == 0 (EINVAL otherwise); N % 256 == 0,
+ * K % 128 == 0 and E <= 2048 (EUNSUPPORTED otherwise).  Accuracy as for the weight
  * gradient: this entry point splits A's codes into two MFMA passes (codes of
  * magnitude >= 128 and the rest), which keeps the result within
  * 2^-7 |ref| + 2^-12 rms(ref) of the exact sum also with 64x outliers in A.

@@ -41,34 +41,27 @@ constexpr int NWAVE = 8;
 constexpr int NTHREAD = NWAVE * 64;
 constexpr int LOADS_PER_STEP = 18;            // stage loads a loading wave issues per step
 
-// One pass of an output tile: token-row tile mt, column tile jt, expert e,
-// whose rows [rlo, rhi) of the tile (relative to m0 = 256 mt) count.
-struct Pass {
-  int valid, t, e, rlo, rhi;
-};
+constexpr int MAX_E = 2048;                   // experts (LDS tables of E + 1 entries)
+constexpr int SCAN_PER = (MAX_E + 1 + NTHREAD - 1) / NTHREAD;   // table entries per thread in the scans
 
-// The expert pass of tile t at or after expert e (the next one with rows in
-// the tile), or none.
-__device__ __forceinline__ Pass pass_from(int t, int e, int total, int tilesJ, const int32_t *__restrict__ off,
-                                          int M, int E) {
-  Pass p;
-  p.valid = 0; p.t = t; p.e = e; p.rlo = 0; p.rhi = 0;
-  if (t >= total) return p;
-  const int m0 = (t / tilesJ) * TN;
-  const int m1 = min(m0 + TN, M);
-  const int e_last = expert_of_row(off, E, m1 - 1);
-  e = max(e, expert_of_row(off, E, m0));      // experts before the one owning m0 hold no rows here
-  for (; e <= e_last; ++e) {
-    const int o0 = clampi(off[e], 0, M);
-    const int o1 = clampi(off[e + 1], o0, M);
-    const int lo = max(o0, m0), hi = min(o1, m1);
-    if (hi > lo) {
-      p.valid = 1; p.e = e; p.rlo = lo - m0; p.rhi = hi - m0;
-      return p;
-    }
+// Inclusive scan over the workgroup's 512 threads (Hillis-Steele through LDS).
+template <bool MAX>
+__device__ __forceinline__ int block_scan(int x, int *red, int tid) {
+#pragma unroll 1
+  for (int d = 1; d < NTHREAD; d <<= 1) {
+    red[tid] = x;
+    barrier();
+    if (tid >= d) x = MAX ? max(x, red[tid - d]) : x + red[tid - d];
+    barrier();
   }
-  return p;
+  return x;
 }
+
+// An output tile: 256 columns jt of up to 256 token rows [m0, m0 + rows)
+// that all belong to expert e (kind 1), or rows of no expert (kind 2).
+struct Tile {
+  int kind, e, jt, m0, rows;
+};
 
 template <bool SPLIT>
 __global__ __launch_bounds__(NTHREAD, 1) void grouped_mxfp8_kernel(
@@ -76,14 +69,94 @@ __global__ __launch_bounds__(NTHREAD, 1) void grouped_mxfp8_kernel(
     const uint8_t *__restrict__ SA, const uint8_t *__restrict__ SB,
     const int32_t *__restrict__ off, int M, int N, int K, int E) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE_BYTES];
+  __shared__ int s_row[MAX_E + 1];    // expert e owns token rows [s_row[e], s_row[e + 1])
+  __shared__ int s_pre[MAX_E + 1];    // row tiles of the experts before e
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tilesM = (M + TN - 1) / TN, tilesJ = N / TK;
-  const int total = tilesM * tilesJ;
-  const int nk = K / TT;                   // contraction steps per pass
+  const int tilesJ = N / TK;
+  const int nk = K / TT;                   // contraction steps per tile
   const int G = gridDim.x;
+
+  // ---- expert row ranges and row-tile prefix (one pass over the offsets) ----
+  // Rows: offsets clamped to [0, M] and made nondecreasing by a running
+  // maximum, so the experts' row ranges are disjoint; for well-formed offsets
+  // this is off itself.  Each expert splits into ceil(rows / 256) row tiles.
+  {
+    int *red = reinterpret_cast<int *>(smem);
+    const int e0 = tid * SCAN_PER;
+    int v[SCAN_PER];
+    int run = 0;
+#pragma unroll
+    for (int j = 0; j < SCAN_PER; ++j) {
+      const int e = e0 + j;
+      if (e <= E) run = max(run, clampi(off[e], 0, M));
+      v[j] = run;
+    }
+    int incl = block_scan<true>(run, red, tid);
+    red[tid] = incl;
+    barrier();
+    const int before = tid ? red[tid - 1] : 0;
+#pragma unroll
+    for (int j = 0; j < SCAN_PER; ++j)
+      if (e0 + j <= E) s_row[e0 + j] = max(before, v[j]);
+    barrier();
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < SCAN_PER; ++j) {
+      const int e = e0 + j;
+      v[j] = e < E ? (s_row[e + 1] - s_row[e] + TN - 1) / TN : 0;
+      cnt += v[j];
+    }
+    incl = block_scan<false>(cnt, red, tid);
+    int pre = incl - cnt;
+#pragma unroll
+    for (int j = 0; j < SCAN_PER; ++j) {
+      if (e0 + j <= E) s_pre[e0 + j] = pre;
+      pre += v[j];
+    }
+    barrier();
+  }
+  const int R = s_pre[E];                                  // expert row tiles
+  const int row_first = s_row[0], row_end = s_row[E];
+  const int Zh = (row_first + TN - 1) / TN;                // row tiles of no expert before / after
+  const int Zt = (M - row_end + TN - 1) / TN;
+  const int expert_tiles = R * tilesJ;
+  const int total = (R + Zh + Zt) * tilesJ;
+
+  // Tile order o: expert-major, then the column tile, then the expert's row
+  // tile, so the workgroups that share a weight tile B[e][j0..] run together;
+  // the rows of no expert come last.  Workgroup b runs o = lb, lb + G, ...
+  // with lb chosen so that the workgroups of one XCD (b mod 8, the dispatch
+  // order) hold consecutive o and share that XCD's L2.
+  auto tile_of = [&](int o) __attribute__((always_inline)) {
+    Tile t;
+    t.kind = 0; t.e = 0; t.jt = 0; t.m0 = 0; t.rows = 0;
+    if (o >= total) return t;
+    if (o < expert_tiles) {
+      int lo = 0, hi = E;                                  // s_pre[lo] * tilesJ <= o < s_pre[hi] * tilesJ
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_pre[mid] * tilesJ <= o) lo = mid; else hi = mid;
+      }
+      const int ce = s_pre[lo + 1] - s_pre[lo];
+      const int r = o - s_pre[lo] * tilesJ;
+      const int jt = r / ce, i = r - jt * ce;
+      t.kind = 1; t.e = lo; t.jt = jt;
+      t.m0 = s_row[lo] + i * TN;
+      t.rows = min(TN, s_row[lo + 1] - t.m0);
+    } else {
+      const int z = o - expert_tiles;
+      const int zr = z / tilesJ;
+      t.kind = 2; t.jt = z - zr * tilesJ;
+      if (zr < Zh) { t.m0 = zr * TN; t.rows = min(TN, row_first - t.m0); }
+      else { t.m0 = row_end + (zr - Zh) * TN; t.rows = min(TN, M - t.m0); }
+    }
+    return t;
+  };
+  const int b = blockIdx.x;
+  const int lb = (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
 
   // ---- per-lane constants -------------------------------------------------
   const uint32_t smem_base = lds_addr(smem);
@@ -110,7 +183,7 @@ __global__ __launch_bounds__(NTHREAD, 1) void grouped_mxfp8_kernel(
 #pragma unroll
   for (int a = 0; a < 4; ++a) xrow[a] = ST_X + tile_row(wk * 128 + a * 32 + l32);
 #pragma unroll
-  for (int b = 0; b < 2; ++b) grow[b] = ST_G + tile_row(wn * 64 + b * 32 + l32);
+  for (int bb = 0; bb < 2; ++bb) grow[bb] = ST_G + tile_row(wn * 64 + bb * 32 + l32);
   uint32_t chunk_off[2][2];   // [half][piece] -> 16-byte chunk offset within the row
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -118,37 +191,27 @@ __global__ __launch_bounds__(NTHREAD, 1) void grouped_mxfp8_kernel(
     chunk_off[h][1] = (4 * h + 2 + g) * 16;
   }
 
-  // the load cursor: pass p, step s; after a tile's last pass, the first pass
-  // of the workgroup's next tile that has one
-  struct Cursor {
-    Pass p;
-    int s;
-  };
-  auto seek = [&](int t) __attribute__((always_inline)) {
-    Pass p = pass_from(t, 0, total, tilesJ, off, M, E);
-    while (t < total && !p.valid) { t += G; p = pass_from(t, 0, total, tilesJ, off, M, E); }
-    return p;
-  };
-  auto advance = [&](Cursor &c) __attribute__((always_inline)) {
-    if (c.s + 1 < nk) { ++c.s; return; }
-    c.s = 0;
-    Pass q = pass_from(c.p.t, c.p.e + 1, total, tilesJ, off, M, E);
-    c.p = q.valid ? q : seek(c.p.t + G);
+  // the load cursor: the workgroup's k-th tile, step s (expert tiles only;
+  // they precede every tile of no expert in the order)
+  int ld_k = 0, ld_s = 0;
+  Tile ld_t = tile_of(lb);
+  auto advance = [&]() __attribute__((always_inline)) {
+    if (++ld_s < nk) return;
+    ld_s = 0;
+    ++ld_k;
+    ld_t = tile_of(lb + ld_k * G);
   };
 
   int ops = 0;               // vector-memory instructions this wave has issued (uniform)
   int mark[2] = {0, 0};      // value of ops right after the loads of the step in buffer 0 / 1
 
-  auto issue_stage = [&](const Cursor &c, uint32_t buf) __attribute__((always_inline)) {
+  auto issue_stage = [&](uint32_t buf) __attribute__((always_inline)) {
     if (!loader) return;
-    const int t = c.p.t;
-    const int mt = t / tilesJ, jt = t - mt * tilesJ;
-    const int m0 = mt * TN;
-    const uint32_t rows = static_cast<uint32_t>(min(TN, M - m0));
-    const uint32_t cpos = static_cast<uint32_t>(c.s * TT);
-    const size_t wrow = static_cast<size_t>(c.p.e) * N + static_cast<size_t>(jt) * TK;   // first weight row
+    const uint32_t cpos = static_cast<uint32_t>(ld_s * TT);
+    const size_t wrow = static_cast<size_t>(ld_t.e) * N + static_cast<size_t>(ld_t.jt) * TK;   // first weight row
+    const uint32_t rows = static_cast<uint32_t>(ld_t.rows);
     const v4i srd_x = make_srd(B + wrow * K, TK * Kb);
-    const v4i srd_g = make_srd(A + static_cast<size_t>(m0) * K, rows * Kb);
+    const v4i srd_g = make_srd(A + static_cast<size_t>(ld_t.m0) * K, rows * Kb);
     const uint32_t base = smem_base + buf * STAGE_BYTES;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -157,15 +220,15 @@ __global__ __launch_bounds__(NTHREAD, 1) void grouped_mxfp8_kernel(
     for (int i = 0; i < 8; ++i)
       dma_b128(srd_g, voff_t[i], cpos, __builtin_amdgcn_readfirstlane(base + ST_G + (w4 * 8 + i) * BLK));
     const v4i srd_sx = make_srd(SB + wrow * scale_row, 256u * scale_row);
-    const v4i srd_sg = make_srd(SA + static_cast<size_t>(m0) * scale_row, rows * scale_row);
+    const v4i srd_sg = make_srd(SA + static_cast<size_t>(ld_t.m0) * scale_row, rows * scale_row);
     dma_b32(srd_sx, voff_s, cpos / 32, __builtin_amdgcn_readfirstlane(base + ST_SX + w4 * 256));
     dma_b32(srd_sg, voff_s, cpos / 32, __builtin_amdgcn_readfirstlane(base + ST_SG + w4 * 256));
     ops += LOADS_PER_STEP;
   };
   // wait until the loads of the step in buffer b have landed: every vector
   // memory instruction issued after them may still be in flight
-  auto wait_step = [&](int b) __attribute__((always_inline)) {
-    const int younger = ops - mark[b];
+  auto wait_step = [&](int bf) __attribute__((always_inline)) {
+    const int younger = ops - mark[bf];
     if (younger >= 50) wait_vmcnt<50>();
     else if (younger >= 34) wait_vmcnt<34>();
     else if (younger >= 18) wait_vmcnt<18>();
@@ -175,55 +238,49 @@ __global__ __launch_bounds__(NTHREAD, 1) void grouped_mxfp8_kernel(
   };
 
   // ---- prologue: first step in flight ----
-  Cursor ld;
-  ld.p = seek(blockIdx.x);
-  ld.s = 0;
-  if (ld.p.valid) {
-    issue_stage(ld, 0);
+  if (ld_t.kind == 1) {
+    issue_stage(0);
     mark[0] = ops;
-    advance(ld);
+    advance();
   }
 
   uint32_t buf = 0;                    // buffer of the step being computed
   v16f acc[4][2];
-  for (int t = blockIdx.x; t < total; t += G) {
+  const uint32_t Nu = static_cast<uint32_t>(N);
+#pragma unroll 1
+  for (int k = 0;; ++k) {
+    const Tile cur = tile_of(lb + k * G);
+    if (cur.kind == 0) break;
+    const __amdgpu_buffer_rsrc_t crsrc = __builtin_amdgcn_make_buffer_rsrc(
+        C + static_cast<size_t>(cur.m0) * N + static_cast<size_t>(cur.jt) * TK, static_cast<short>(0),
+        static_cast<int>((static_cast<uint32_t>(cur.rows - 1) * Nu + TK) * 2u), 0x00020000);
+    if (cur.kind == 2) {                                  // rows of no expert: +0.0
+      store_zero_tile(crsrc, Nu, tid);
+      ops += STORES_PER_TILE;
+      continue;
+    }
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+      for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
-
-    Pass cur = pass_from(t, 0, total, tilesJ, off, M, E);
-    const bool any = cur.valid;
+        for (int i = 0; i < 16; ++i) acc[a][bb][i] = 0.f;
 #pragma unroll 1
-    while (cur.valid) {
-#pragma unroll 1
-      for (int s = 0; s < nk; ++s) {
-        wait_step(buf);
-        barrier();
-        if (ld.p.valid) {
-          issue_stage(ld, buf ^ 1);
-          mark[buf ^ 1] = ops;
-          advance(ld);
-        }
-        const uint8_t *st = smem + buf * STAGE_BYTES;
-        compute_step<SPLIT>(st, acc, xrow, grow, chunk_off, wk, wn, l32, g, 0, TT, cur.rlo, cur.rhi);
-        buf ^= 1;
+    for (int s = 0; s < nk; ++s) {
+      wait_step(buf);
+      barrier();
+      if (ld_t.kind == 1) {
+        issue_stage(buf ^ 1);
+        mark[buf ^ 1] = ops;
+        advance();
       }
-      cur = pass_from(t, cur.e + 1, total, tilesJ, off, M, E);
+      const uint8_t *st = smem + buf * STAGE_BYTES;
+      compute_step<SPLIT>(st, acc, xrow, grow, chunk_off, wk, wn, l32, g, 0, TT, 0, TN);
+      buf ^= 1;
     }
-
-    // ---- epilogue: C[m0 + m][j0 + j], rows past M dropped by the descriptor
-    const int mt = t / tilesJ, jt = t - mt * tilesJ;
-    const int m0 = mt * TN;
-    const uint32_t Nu = static_cast<uint32_t>(N);
-    const uint32_t rows = static_cast<uint32_t>(min(TN, M - m0));
-    const __amdgpu_buffer_rsrc_t crsrc = __builtin_amdgcn_make_buffer_rsrc(
-        C + static_cast<size_t>(m0) * N + static_cast<size_t>(jt) * TK, static_cast<short>(0),
-        static_cast<int>(((rows - 1u) * Nu + TK) * 2u), 0x00020000);
-    if (!any) store_zero_tile(crsrc, Nu, tid);            // rows of no expert: +0.0
-    else store_tile(acc, smem + (buf ^ 1) * STAGE_BYTES, crsrc, Nu, wk, wn, tid);
+    // ---- epilogue: C[m0 + m][j0 + j] for the tile's rows; the descriptor
+    // drops the rest
+    store_tile(acc, smem + (buf ^ 1) * STAGE_BYTES, crsrc, Nu, wk, wn, tid);
     ops += STORES_PER_TILE;
   }
   wait_vmcnt<0>();
@@ -235,7 +292,7 @@ int launch_grouped(bool split, const uint8_t *A, const uint8_t *B, uint16_t *C, 
   if (!A || !B || !C || !scale_A || !scale_B || !expert_off) return MOE_GG_EINVAL;
   if (M <= 0 || N <= 0 || K <= 0 || E <= 0) return MOE_GG_EINVAL;
   if (K % 32) return MOE_GG_EINVAL;
-  if (N % TK || K % TT) return MOE_GG_EUNSUPPORTED;
+  if (N % TK || K % TT || E > MAX_E) return MOE_GG_EUNSUPPORTED;
   // 32-bit byte offsets inside one 256-row panel and inside a tile of C
   if (static_cast<uint64_t>(TN) * static_cast<uint64_t>(K) > 0xFFFFFFFFull) return MOE_GG_EUNSUPPORTED;
   if (static_cast<uint64_t>(TN) * static_cast<uint64_t>(N) * 2u > 0x7FFFFFFFull) return MOE_GG_EUNSUPPORTED;
@@ -243,7 +300,9 @@ int launch_grouped(bool split, const uint8_t *A, const uint8_t *B, uint16_t *C, 
   if (hipGetDevice(&dev) != hipSuccess) return MOE_GG_ELAUNCH;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     return MOE_GG_ELAUNCH;
-  const int64_t total = static_cast<int64_t>((M + TN - 1) / TN) * (N / TK);
+  // row tiles: at most one partial tile per expert beyond ceil(M / 256), plus
+  // the rows of no expert before and after
+  const int64_t total = (static_cast<int64_t>((M + TN - 1) / TN) + E + 2) * (N / TK);
   if (total > 0x7FFFFFFF) return MOE_GG_EUNSUPPORTED;
   const int grid = static_cast<int>(total < cus ? total : cus);
   if (split)

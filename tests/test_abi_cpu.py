@@ -82,6 +82,8 @@ def test_host_validation_grouped(lib, name):
     assert f(p, p, p, p, p, p, 300, 256, 48, 3, None) == -1        # K % 32
     assert f(p, p, p, p, p, p, 300, 200, 256, 3, None) == -2       # N % 256
     assert f(p, p, p, p, p, p, 300, 256, 160, 3, None) == -2       # K % 128
+    assert f(p, p, p, p, p, p, 300, 256, 256, 2049, None) == -2    # E > 2048 (LDS tables)
+    assert f(p, p, p, p, p, p, 300, 256, 256, 2048, None) not in (-1, -2)
 
 
 def test_host_validation_dgrad_quantize_rows(lib):

@@ -145,3 +145,76 @@ def test_grouped_larger_sampled():
     ref = oracle.grouped_gemm_rows(ca, sa, cb, sb, off, rows)
     out = host(got[rows]).astype(np.float64)
     assert oracle.wgrad_excess(out, ref, ref_rms=np.sqrt(np.mean(ref * ref))) <= 0
+
+
+def test_grouped_rows_of_no_expert_are_zero():
+    """off[0] > 0 and off[E] < M: the rows before and after every expert are +0.0, the rest unchanged."""
+    torch, mg = require_gpu()
+    rng = np.random.default_rng(5)
+    off = np.array([64, 300, 300, 555], np.int32)
+    M, N, K, E = 900, 512, 256, 3
+    ca, sa = oracle.mx_quantize(rng.standard_normal((M, K)).astype(np.float32))
+    cb, sb = _quant_b(rng.standard_normal((E, N, K)).astype(np.float32))
+    say("grouped rows of no expert", list(off), M)
+    out = mg.grouped_mxfp8(dev(torch, ca), dev(torch, cb), dev(torch, sa), dev(torch, sb), dev(torch, off))
+    torch.cuda.synchronize()
+    got = host(out).astype(np.float64)
+    bits = host(out.view(torch.int16))
+    assert np.all(bits[:64] == 0) and np.all(bits[555:] == 0)       # +0.0, not -0.0
+    inner = oracle.grouped_gemm(ca[64:555], sa[64:555], cb, sb, off - 64)
+    assert oracle.wgrad_excess(got[64:555], inner) <= 0
+
+
+def test_grouped_most_experts():
+    """E = 2048 (the limit of the on-chip offset tables), 0..6 tokens each."""
+    torch, mg = require_gpu()
+    rng = np.random.default_rng(2048)
+    E, N, K = 2048, 256, 128
+    counts = rng.integers(0, 7, size=E)
+    counts[:5] = 0
+    counts[-3:] = 0
+    off = wl.offsets_from_counts(counts)
+    M = int(off[-1])
+    ca, sa = oracle.mx_quantize(rng.standard_normal((M, K)).astype(np.float32))
+    cb, sb = _quant_b(rng.standard_normal((E, N, K)).astype(np.float32))
+    say("grouped E=2048", M)
+    got = _run(torch, mg, ca, sa, cb, sb, off)
+    ref = oracle.grouped_gemm(ca, sa, cb, sb, off)
+    assert oracle.wgrad_excess(got, ref) <= 0
+
+
+def test_grouped_full_size_data_gradient_sampled():
+    """The 64-expert data gradient at full size (M=16384, contraction 1536, 7168 outputs, the offsets
+    and g of that workload): sampled rows of ten experts against the oracle.  B[e] is one of four
+    MX-quantised W_e^T draws, rolled along its rows by a per-expert amount, so experts differ."""
+    torch, mg = require_gpu()
+    w = wl.WORKLOADS[5]
+    rng = np.random.default_rng(5)
+    off = wl.make_offsets(5, rng)
+    g = rng.standard_normal((w.M, w.N), dtype=np.float32) * np.float32(0.02)
+    ca, sa = oracle.mx_quantize(g)                                   # along the contraction N
+    del g
+    wrng = np.random.default_rng(55)
+    base = [oracle.mx_quantize(wrng.standard_normal((w.K, w.N), dtype=np.float32) * np.float32(0.02))
+            for _ in range(4)]
+    cb = np.empty((w.E, w.K, w.N), np.uint8)
+    sb = np.empty((w.E, w.K, w.N // 32), np.uint8)
+    for e in range(w.E):
+        q, s = base[e % 4]
+        cb[e] = np.roll(q, 37 * e, axis=0)
+        sb[e] = np.roll(s, 37 * e, axis=0)
+    say("grouped full-size data gradient, workload 5", w)
+    got = mg.grouped_mxfp8(dev(torch, ca), dev(torch, cb), dev(torch, sa), dev(torch, sb), dev(torch, off))
+    torch.cuda.synchronize()
+    assert tuple(got.shape) == (w.M, w.K)
+    counts = np.diff(off)
+    nonempty = np.flatnonzero(counts)
+    picked = np.unique(np.concatenate([nonempty[:2], nonempty[-2:], rng.choice(nonempty, 6, replace=False)]))
+    rows = []
+    for e in picked:
+        o0, o1 = int(off[e]), int(off[e + 1])
+        rows.append(o0 + sample_rows(rng, o1 - o0, 6, must=(0, 255, 256, o1 - o0 - 1)))
+    rows = np.concatenate(rows)
+    ref = oracle.grouped_gemm_rows(ca, sa, cb, sb, off, rows)
+    out = host(got[rows]).astype(np.float64)
+    assert oracle.wgrad_excess(out, ref, ref_rms=np.sqrt(np.mean(ref * ref))) <= 0
