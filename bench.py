@@ -146,7 +146,7 @@ def bench_wgrad(torch, mg, idx, steps, warmup, cpu_baseline, fast=False):
                    "tokens_per_expert": [int(c) for c in np.diff(off_np)]},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_FP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP8_TFLOPS, 4),
-                     "traffic": read_traffic("wgrad", idx),
+                     "traffic": None if fast else read_traffic("wgrad", idx),
                      "algorithmic_bytes": algo_bytes, "algorithmic_flop": flop,
                      "hbm_gbs_algorithmic": round(algo_bytes / (ms * 1e-3) / 1e9, 1)},
     }
@@ -236,7 +236,8 @@ def bench_grouped(torch, mg, idx, steps, warmup, cpu_baseline, fast=False):
             "mode": "single block-scaled MFMA pass" if fast else "two block-scaled MFMA passes (A codes >= 128 / the rest)",
             "config": {"workload": wl.WORKLOADS[idx].name, "E": E, "M": M, "contraction": N, "N_out": K},
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tf / PEAK_FP8_TFLOPS, 4), "traffic": None,
+                         "frac": round(tf / PEAK_FP8_TFLOPS, 4),
+                         "traffic": None if fast else read_traffic("grouped", idx),
                          "algorithmic_bytes": int(nbytes), "algorithmic_flop": flop}}
     if cpu_baseline:
         import oracle
