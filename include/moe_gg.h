@@ -207,6 +207,26 @@ MOE_GG_API int moe_gg_mx_quantize_t(const float *X, uint8_t *Q, uint8_t *S, int 
                                     hipStream_t stream);
 
 /*
+ * The two quantisers with the round-up scale rule instead of the floor rule.
+ *
+ * Source: the decode page's mx8_scale ("aiter's MXFP8 RoundUp rule"): the
+ * scale is ceil_pow2(max / 448), the quotient formed in f32 as the product
+ * of the block max and f32(1/448); the byte is that product's exponent field
+ * plus one if its mantissa is nonzero, clamped to [1, 254].
+ *
+ *   t = f32(max |block| * f32(1/448));  s = clamp(ceil(log2 t) + 127, 1, 254)
+ *   (s = 1 for a zero block); codes as above: e4m3_rne_saturate(X * 2^(127 - s))
+ *
+ * The block max lands in (224, 448] after scaling (448 (1 + 2^-22) at the f32
+ * edge, saturated), so no element saturates beyond rounding.  Same layouts,
+ * shapes and status codes as moe_gg_mx_quantize / moe_gg_mx_quantize_t.
+ */
+MOE_GG_API int moe_gg_mx_quantize_roundup(const float *X, uint8_t *Q, uint8_t *S, int R, int L,
+                                          hipStream_t stream);
+MOE_GG_API int moe_gg_mx_quantize_t_roundup(const float *X, uint8_t *Q, uint8_t *S, int R, int L,
+                                            hipStream_t stream);
+
+/*
  * Row -> expert map, the integer step of the data gradient, exposed so that
  * it can be checked exactly: out[r] = the e with off[e] <= r < off[e+1] for r
  * in [0, M), computed by the same device function the data-gradient kernel

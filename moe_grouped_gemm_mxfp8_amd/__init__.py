@@ -7,8 +7,8 @@ memory and the current stream, nothing else):
   wgrad_mxfp8(a, b, scale_a, scale_b, expert_off, out=None, fast=False) -> bf16 [E*N, K]
   grouped_mxfp8(a, b, scale_a, scale_b, expert_off, out=None, fast=False) -> bf16 [M, N]
   dgrad_f32(g, w, expert_off, out=None)                     -> f32 [M, K]
-  mx_quantize(x, q=None, s=None)                            -> (uint8 [R, L], uint8 [R, L/32])
-  mx_quantize_t(x, q=None, s=None)                          -> (uint8 [L, R], uint8 [L, R/32])
+  mx_quantize(x, q=None, s=None, rule="floor")              -> (uint8 [R, L], uint8 [R, L/32])
+  mx_quantize_t(x, q=None, s=None, rule="floor")            -> (uint8 [L, R], uint8 [L, R/32])
   row_experts(expert_off, M, out=None)                      -> int32 [M]
 
 There is no CPU fallback: calling any of them without the built library or

@@ -8,6 +8,12 @@
 // E4M3, ties to even, saturating at +-448 (the decode page's mx8_q clamps to
 // +-FP8_MAX before its conversion), sign of zero kept.
 //
+// Round-up rule (the *_roundup entry points; the decode page's mx8_scale):
+// the smallest power of two not below t = max * f32(1/448), t rounded to f32
+// (v_mul_f32), read from t's bits as its exponent field plus one when its
+// mantissa is nonzero, clamped to [1, 254].  The block max then lands in
+// (224, 448] after scaling, so nothing saturates beyond rounding.
+//
 // The E4M3 rounding is the hardware's: v_cvt_pk_fp8_f32 rounds to nearest
 // even, keeps the sign of zero and produces E4M3 subnormals, and matches the
 // oracle code for code on every value up to 464 (measured on gfx950); above
@@ -41,7 +47,13 @@ __device__ __forceinline__ int floor_log2_bits(uint32_t a /* |x| bits, nonzero *
   return (31 - __clz(a)) - 149;          // f32 subnormal: value = a * 2^-149
 }
 
+template <bool ROUNDUP>
 __device__ __forceinline__ uint32_t scale_byte(uint32_t amax_bits) {
+  if (ROUNDUP) {
+    const uint32_t t = __float_as_uint(__uint_as_float(amax_bits) * (1.0f / 448.0f));
+    const int e = static_cast<int>(t >> 23) + ((t & 0x7FFFFFu) != 0u ? 1 : 0);
+    return static_cast<uint32_t>(e < 1 ? 1 : (e > 254 ? 254 : e));
+  }
   if (amax_bits == 0) return 1u;
   const int s = floor_log2_bits(amax_bits) - 8 + 127;
   return static_cast<uint32_t>(s < 1 ? 1 : (s > 254 ? 254 : s));
@@ -59,6 +71,7 @@ __device__ __forceinline__ uint32_t e4m3x4(v4f v, uint32_t sb) {
   return static_cast<uint32_t>(w);
 }
 
+template <bool ROUNDUP>
 __global__ __launch_bounds__(256) void mx_quantize_kernel(const float *__restrict__ X, uint8_t *__restrict__ Q,
                                                           uint8_t *__restrict__ S, int64_t total) {
   const int lane = threadIdx.x & 63;
@@ -76,7 +89,7 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(const float *__restric
       m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 1)));
       m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 2)));
       m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 4)));
-      const uint32_t sb = scale_byte(m);
+      const uint32_t sb = scale_byte<ROUNDUP>(m);
       const uint32_t word = e4m3x4(v, sb);
       if (live) {
         __builtin_nontemporal_store(word, reinterpret_cast<uint32_t *>(Q + i0));
@@ -90,6 +103,7 @@ constexpr int QT_TOK = 128;                // tokens per transposed tile
 constexpr int QT_FEAT = 64;                // features per transposed tile
 constexpr int QT_PITCH = QT_TOK + 4;       // floats per LDS feature row
 
+template <bool ROUNDUP>
 __global__ __launch_bounds__(256) void mx_quantize_t_kernel(const float *__restrict__ X, uint8_t *__restrict__ Q,
                                                             uint8_t *__restrict__ S, int R, int L, int tiles_f) {
   __shared__ __attribute__((aligned(16))) float tile[QT_FEAT * QT_PITCH];
@@ -121,7 +135,7 @@ __global__ __launch_bounds__(256) void mx_quantize_t_kernel(const float *__restr
 #pragma unroll
     for (int j = 0; j < 4; ++j) m = max(m, __float_as_uint(v[i][j]) & 0x7FFFFFFFu);
   }
-  const uint32_t sb = scale_byte(m);
+  const uint32_t sb = scale_byte<ROUNDUP>(m);
   v4u lo, hi;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -134,25 +148,22 @@ __global__ __launch_bounds__(256) void mx_quantize_t_kernel(const float *__restr
   S[static_cast<size_t>(gf) * (R / 32) + gt / 32] = static_cast<uint8_t>(sb);
 }
 
-}  // namespace
-}  // namespace moe_gg
-
-extern "C" MOE_GG_API int moe_gg_mx_quantize_t(const float *X, uint8_t *Q, uint8_t *S, int R, int L,
-                                               hipStream_t stream) {
-  using namespace moe_gg;
+int launch_quantize_t(bool roundup, const float *X, uint8_t *Q, uint8_t *S, int R, int L, hipStream_t stream) {
   if (!X || !Q || !S || R <= 0 || L <= 0 || R % 32) return MOE_GG_EINVAL;
   if (L % 4) return MOE_GG_EUNSUPPORTED;
   const int tiles_t = (R + QT_TOK - 1) / QT_TOK, tiles_f = (L + QT_FEAT - 1) / QT_FEAT;
   const int64_t blocks = static_cast<int64_t>(tiles_t) * tiles_f;
   if (blocks > 0x7FFFFFFF) return MOE_GG_EUNSUPPORTED;
-  hipLaunchKernelGGL(mx_quantize_t_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, X, Q, S, R, L,
-                     tiles_f);
+  if (roundup)
+    hipLaunchKernelGGL(mx_quantize_t_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, X, Q,
+                       S, R, L, tiles_f);
+  else
+    hipLaunchKernelGGL(mx_quantize_t_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, X, Q,
+                       S, R, L, tiles_f);
   return hipGetLastError() == hipSuccess ? MOE_GG_OK : MOE_GG_ELAUNCH;
 }
 
-extern "C" MOE_GG_API int moe_gg_mx_quantize(const float *X, uint8_t *Q, uint8_t *S, int R, int L,
-                                             hipStream_t stream) {
-  using namespace moe_gg;
+int launch_quantize(bool roundup, const float *X, uint8_t *Q, uint8_t *S, int R, int L, hipStream_t stream) {
   if (!X || !Q || !S || R <= 0 || L < 32 || L % 32) return MOE_GG_EINVAL;
   const int64_t total = static_cast<int64_t>(R) * L;
   int dev = 0, cus = 0;
@@ -163,6 +174,34 @@ extern "C" MOE_GG_API int moe_gg_mx_quantize(const float *X, uint8_t *Q, uint8_t
   int64_t blocks = (waves_needed + 3) / 4;
   const int64_t cap = static_cast<int64_t>(cus) * 16;
   if (blocks > cap) blocks = cap;
-  hipLaunchKernelGGL(mx_quantize_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, X, Q, S, total);
+  if (roundup)
+    hipLaunchKernelGGL(mx_quantize_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, X, Q, S,
+                       total);
+  else
+    hipLaunchKernelGGL(mx_quantize_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, X, Q, S,
+                       total);
   return hipGetLastError() == hipSuccess ? MOE_GG_OK : MOE_GG_ELAUNCH;
+}
+
+}  // namespace
+}  // namespace moe_gg
+
+extern "C" MOE_GG_API int moe_gg_mx_quantize_t(const float *X, uint8_t *Q, uint8_t *S, int R, int L,
+                                               hipStream_t stream) {
+  return moe_gg::launch_quantize_t(false, X, Q, S, R, L, stream);
+}
+
+extern "C" MOE_GG_API int moe_gg_mx_quantize_t_roundup(const float *X, uint8_t *Q, uint8_t *S, int R, int L,
+                                                       hipStream_t stream) {
+  return moe_gg::launch_quantize_t(true, X, Q, S, R, L, stream);
+}
+
+extern "C" MOE_GG_API int moe_gg_mx_quantize(const float *X, uint8_t *Q, uint8_t *S, int R, int L,
+                                             hipStream_t stream) {
+  return moe_gg::launch_quantize(false, X, Q, S, R, L, stream);
+}
+
+extern "C" MOE_GG_API int moe_gg_mx_quantize_roundup(const float *X, uint8_t *Q, uint8_t *S, int R, int L,
+                                                     hipStream_t stream) {
+  return moe_gg::launch_quantize(true, X, Q, S, R, L, stream);
 }

@@ -101,8 +101,21 @@ def grouped_mxfp8(a, b, scale_a, scale_b, expert_off, out=None, fast=False):
     return out
 
 
-def mx_quantize(x, q=None, s=None):
-    """MX-quantise f32 x[R, L] along L: (E4M3 codes uint8 [R, L], E8M0 scales uint8 [R, L/32])."""
+_RULES = {"floor": "", "roundup": "_roundup"}
+
+
+def _rule_suffix(rule):
+    if rule not in _RULES:
+        raise ValueError("rule must be 'floor' or 'roundup'")
+    return _RULES[rule]
+
+
+def mx_quantize(x, q=None, s=None, rule="floor"):
+    """MX-quantise f32 x[R, L] along L: (E4M3 codes uint8 [R, L], E8M0 scales uint8 [R, L/32]).
+
+    rule: "floor" (2^(floor(log2 max) - 8)) or "roundup" (ceil_pow2(max / 448)).
+    """
+    suffix = _rule_suffix(rule)
     _dev(x, "x", (torch.float32,))
     if x.dim() != 2:
         raise ValueError("x must be [R, L]")
@@ -112,12 +125,13 @@ def mx_quantize(x, q=None, s=None):
     if s is None:
         s = torch.empty((R, max(L // 32, 1)), dtype=torch.uint8, device=x.device)
     _dev(q, "q", _U8); _dev(s, "s", _U8)
-    call("moe_gg_mx_quantize", x.data_ptr(), q.data_ptr(), s.data_ptr(), R, L, _stream())
+    call("moe_gg_mx_quantize" + suffix, x.data_ptr(), q.data_ptr(), s.data_ptr(), R, L, _stream())
     return q, s
 
 
-def mx_quantize_t(x, q=None, s=None):
+def mx_quantize_t(x, q=None, s=None, rule="floor"):
     """MX-quantise the transpose of f32 x[R, L] along R: (codes uint8 [L, R], scales uint8 [L, R/32])."""
+    suffix = _rule_suffix(rule)
     _dev(x, "x", (torch.float32,))
     if x.dim() != 2:
         raise ValueError("x must be [R, L]")
@@ -129,7 +143,7 @@ def mx_quantize_t(x, q=None, s=None):
     _dev(q, "q", _U8); _dev(s, "s", _U8)
     if q.shape != (L, R) or s.shape != (L, max(R // 32, 1)):
         raise ValueError("q must be [L, R] and s [L, R/32]")
-    call("moe_gg_mx_quantize_t", x.data_ptr(), q.data_ptr(), s.data_ptr(), R, L, _stream())
+    call("moe_gg_mx_quantize_t" + suffix, x.data_ptr(), q.data_ptr(), s.data_ptr(), R, L, _stream())
     return q, s
 
 

@@ -26,13 +26,16 @@ off[e] <= m < off[e+1] (half-open, so an empty expert owns nothing).
   mfma_f8f8: fp8 weights with one E8M0 scale per 32 along k, times fp8
   activations):
       C[r, j] = sum_c A[r, c] * B[e(r), j, c]
-  with A and B dequantised, one fp64 matmul per expert segment.
+  with A and B dequantised, one fp64 matmul per expert segment.  B may
+  also be MXFP4 (``b_format="e2m1"``, the decode page's a8w4: fp4 weights
+  times MXFP8 activations); it is then dequantised by the MXFP4 codec.
 """
 from __future__ import annotations
 
 import numpy as np
 
 from .mx import mx_dequantize
+from .mx4 import mx4_dequantize
 
 __all__ = ["check_offsets", "row_experts", "wgrad", "wgrad_rows",
            "wgrad_from_dequantized", "dgrad", "dgrad_rows",
@@ -147,17 +150,28 @@ def dgrad_rows(g, W, off, rows) -> np.ndarray:
     return out
 
 
-def grouped_gemm(codes_a, scales_a, codes_b, scales_b, off) -> np.ndarray:
+def _deq_b(codes_b, scales_b, b_format):
+    if b_format == "e4m3":
+        return mx_dequantize(codes_b, scales_b)
+    if b_format == "e2m1":
+        return mx4_dequantize(codes_b, scales_b)
+    raise ValueError("b_format must be 'e4m3' or 'e2m1'")
+
+
+def grouped_gemm(codes_a, scales_a, codes_b, scales_b, off, b_format: str = "e4m3") -> np.ndarray:
     """Expert-grouped MX GEMM, fp64 [M, N].
 
     codes_a/scales_a: A as E4M3 [M, K] and E8M0 [M, K/32] (token rows);
-    codes_b/scales_b: B as E4M3 [E, N, K] and E8M0 [E, N, K/32].
+    codes_b/scales_b: B as E4M3 [E, N, K] (or, b_format "e2m1", packed E2M1
+    [E, N, K/2]) and E8M0 [E, N, K/32].
     C[r] = deq(A)[r] @ deq(B[e(r)]).T for the expert e(r) that owns row r.
     """
     codes_a = np.asarray(codes_a)
     codes_b = np.asarray(codes_b)
     M, K = codes_a.shape
     E, N, Kb = codes_b.shape
+    if b_format == "e2m1":
+        Kb *= 2
     if Kb != K:
         raise ValueError("A and B must share the contraction axis")
     off = check_offsets(off, M)
@@ -168,11 +182,11 @@ def grouped_gemm(codes_a, scales_a, codes_b, scales_b, off) -> np.ndarray:
     for e in range(E):
         o0, o1 = int(off[e]), int(off[e + 1])
         if o1 > o0:
-            out[o0:o1] = a[o0:o1] @ mx_dequantize(codes_b[e], scales_b[e]).T
+            out[o0:o1] = a[o0:o1] @ _deq_b(codes_b[e], scales_b[e], b_format).T
     return out
 
 
-def grouped_gemm_rows(codes_a, scales_a, codes_b, scales_b, off, rows) -> np.ndarray:
+def grouped_gemm_rows(codes_a, scales_a, codes_b, scales_b, off, rows, b_format: str = "e4m3") -> np.ndarray:
     """Rows ``rows`` of the grouped MX GEMM, fp64 [len(rows), N]; each row uses its own expert."""
     M = np.asarray(codes_a).shape[0]
     rows = np.asarray(rows, dtype=np.int64)
@@ -181,5 +195,5 @@ def grouped_gemm_rows(codes_a, scales_a, codes_b, scales_b, off, rows) -> np.nda
     out = np.empty((rows.size, np.asarray(codes_b).shape[1]), dtype=np.float64)
     for e in np.unique(experts):
         sel = experts == e
-        out[sel] = a[sel] @ mx_dequantize(codes_b[e], scales_b[e]).T
+        out[sel] = a[sel] @ _deq_b(codes_b[e], scales_b[e], b_format).T
     return out

@@ -20,6 +20,13 @@ written from the definitions, in fp64, with no blocking or bit tricks:
   divided by the scale (exact: a power of two) and rounded to the nearest
   E4M3 value, ties to the even code, saturating at +-448 (the decode page's
   ``mx8_q`` clamps to +-FP8_MAX before converting); the sign of zero is kept.
+* The round-up scale rule (the decode page's ``mx8_scale``, "aiter's MXFP8
+  RoundUp rule"): the scale is the smallest power of two not below
+  block_max / 448, where that quotient is the f32 product of the block max
+  and the f32 nearest to 1/448 (the page computes it in f32, and that f32
+  value decides the integer byte, so the oracle takes the same f32 product);
+  the byte is clamped to [1, 254].  The elements are then rounded exactly as
+  under the default rule.
 """
 from __future__ import annotations
 
@@ -28,7 +35,7 @@ import math
 import numpy as np
 
 __all__ = ["e4m3_value", "E4M3_VALUES", "E4M3_MAX", "e8m0_value",
-           "round_to_e4m3", "mx_scale_bytes", "mx_quantize", "mx_dequantize",
+           "round_to_e4m3", "mx_scale_bytes", "mx_scale_bytes_roundup", "mx_quantize", "mx_dequantize",
            "MX_BLOCK"]
 
 MX_BLOCK = 32          # elements per E8M0 scale along the contiguous axis
@@ -103,12 +110,33 @@ def mx_scale_bytes(block_max) -> np.ndarray:
     return np.where(amax == 0.0, 1, byte).astype(np.uint8)
 
 
-def mx_quantize(x) -> tuple[np.ndarray, np.ndarray]:
+def mx_scale_bytes_roundup(block_max) -> np.ndarray:
+    """E8M0 byte of blocks by the round-up rule: the smallest power of two 2^e
+    with 2^e >= t, t = f32(block_max) * f32(1/448) rounded to f32; byte e + 127
+    clamped to [1, 254] (a zero block gets 1).
+
+    The power of two is read from ``frexp`` in fp64 (exact for an f32 t):
+    t = f * 2^ex with f in [0.5, 1); t is itself a power of two when f = 0.5
+    (then e = ex - 1), otherwise the next one up is 2^ex.
+    """
+    amax = np.asarray(block_max, dtype=np.float64)
+    t = np.asarray(amax.astype(np.float32) * np.float32(1.0 / E4M3_MAX), dtype=np.float32)
+    f, ex = np.frexp(t.astype(np.float64))
+    e = np.where(f == 0.5, ex.astype(np.int64) - 1, ex.astype(np.int64))
+    byte = np.clip(e + 127, 1, 254)
+    return np.where(t == 0.0, 1, byte).astype(np.uint8)
+
+
+def mx_quantize(x, rule: str = "floor") -> tuple[np.ndarray, np.ndarray]:
     """MX-quantise a [R, L] array along its last (contiguous) axis.
 
     Returns ``(codes uint8 [R, L], scales uint8 [R, L/32])``; block j of row r
-    holds elements 32j..32j+31, aligned to the start of the row.
+    holds elements 32j..32j+31, aligned to the start of the row.  ``rule``:
+    "floor" (2^(floor(log2 max) - 8), the default) or "roundup" (the smallest
+    power of two not below max / 448, computed in f32 as the decode page does).
     """
+    if rule not in ("floor", "roundup"):
+        raise ValueError("rule must be 'floor' or 'roundup'")
     x = np.asarray(x)
     if x.ndim != 2 or x.shape[1] % MX_BLOCK:
         raise ValueError("mx_quantize wants [R, L] with L a multiple of 32")
@@ -116,7 +144,8 @@ def mx_quantize(x) -> tuple[np.ndarray, np.ndarray]:
     xb = x.astype(np.float64).reshape(R, L // MX_BLOCK, MX_BLOCK)
     if not np.all(np.isfinite(xb)):
         raise ValueError("non-finite input to mx_quantize")
-    scales = mx_scale_bytes(np.abs(xb).max(axis=2))
+    amax = np.abs(xb).max(axis=2)
+    scales = mx_scale_bytes(amax) if rule == "floor" else mx_scale_bytes_roundup(amax)
     y = xb * np.ldexp(1.0, 127 - scales.astype(np.int64))[..., None]
     codes = round_to_e4m3(y).reshape(R, L)
     return codes, scales

@@ -103,6 +103,48 @@ def test_quantize_transposed_workload_operand():
     assert np.array_equal(host(q), want_q)
 
 
+def _roundup_edges():
+    """Blocks whose max sits on or one f32 ulp either side of 448 * 2^k (where the f32 product
+    decides the byte), plus the default edge blocks."""
+    x = _edge_input()
+    rng = np.random.default_rng(31)
+    rows = []
+    for k in (-20, -1, 0, 3, 40):
+        base = np.float32(448.0 * 2.0 ** k)
+        for m in (np.nextafter(base, np.float32(0)), base, np.nextafter(base, np.float32(np.inf))):
+            blk = (rng.standard_normal(128) * float(base) / 8).astype(np.float32)
+            blk[::32] = -m
+            rows.append(blk)
+    rows.append(np.zeros(128, np.float32))                   # 28 rows: the transposing quantiser wants L % 4 == 0
+    return np.concatenate([x, np.stack(rows)])
+
+
+@pytest.mark.parametrize("case", ["edges", "random"])
+def test_quantize_roundup_bit_exact(case):
+    """Both quantisers with the round-up scale rule equal the oracle's round-up quantisation."""
+    torch, mg = require_gpu()
+    rng = np.random.default_rng(41)
+    if case == "edges":
+        x = _roundup_edges()
+    else:
+        x = (rng.standard_normal((160, 96)) * np.exp2(rng.integers(-60, 60, (160, 1)))).astype(np.float32)
+        x[rng.random(x.shape) < 0.02] *= 64
+    say("quantize roundup", case, x.shape)
+    want_q, want_s = oracle.mx_quantize(x, rule="roundup")
+    q, s = mg.mx_quantize(dev(torch, x), rule="roundup")
+    torch.cuda.synchronize()
+    assert np.array_equal(host(s), want_s)
+    assert np.array_equal(host(q), want_q)
+    xt = np.ascontiguousarray(x.T)                          # quantise_t of x^T is along x's rows
+    q, s = mg.mx_quantize_t(dev(torch, xt), rule="roundup")
+    torch.cuda.synchronize()
+    assert np.array_equal(host(s), want_s)
+    assert np.array_equal(host(q), want_q)
+    # the default rule is unchanged by the variant's existence, and differs from it here
+    fq, fs = oracle.mx_quantize(x)
+    assert not np.array_equal(fs, want_s)
+
+
 OFFSETS = [
     [0, 256],
     [0, 0, 0, 100, 100, 256],

@@ -215,3 +215,84 @@ def test_quantiser_rejects_bad_shapes():
         oracle.mx_quantize(np.zeros((2, 33), np.float32))
     with pytest.raises(ValueError):
         oracle.mx_quantize(np.array([[np.inf] + [0.0] * 31], np.float32))
+
+
+# ---- the round-up scale rule (the decode page's mx8_scale) -----------------
+
+def _exact_roundup_byte(amax):
+    """127 + the exponent of the smallest power of two >= amax / 448, in exact rational arithmetic."""
+    from fractions import Fraction
+    q = Fraction(amax) / 448
+    e = 0
+    while Fraction(2) ** e < q:
+        e += 1
+    while Fraction(2) ** (e - 1) >= q:
+        e -= 1
+    return min(max(e + 127, 1), 254)
+
+
+@pytest.mark.parametrize("k", [-100, -20, -1, 0, 1, 9, 60, 110])
+def test_roundup_exact_multiples_of_448(k):
+    # amax = 448 * 2^k is itself 2^k units of 448: the scale is 2^k whichever way f32(1/448)
+    # rounds (its relative error is below half an ulp of the product), and the max maps to 448
+    amax = 448.0 * 2.0 ** k
+    assert oracle.mx_scale_bytes_roundup([amax])[0] == 127 + k
+    blk = np.zeros((1, 32), np.float32)
+    blk[0, 3] = -amax
+    codes, scales = oracle.mx_quantize(blk, rule="roundup")
+    assert scales[0, 0] == 127 + k and codes[0, 3] == 0xFE          # -448
+
+
+def test_roundup_worked_values():
+    # hand-evaluated: 449/448 > 1 -> 2^1; 447/448 -> 2^0; 1/448 in (2^-9, 2^-8) -> 2^-8;
+    # 3e38/448 = 6.70e35 in (2^119, 2^120) -> 2^120; zero and tiny blocks clamp to 1
+    got = oracle.mx_scale_bytes_roundup([449.0, 447.0, 1.0, 3.0e38, 0.0, 1e-40, 2.0 ** -120])
+    assert list(got) == [128, 127, 119, 247, 1, 1, 1]
+
+
+def test_roundup_against_exact_rule_and_floor_rule():
+    """Away from the f32 edge (block max within 2^-20 of 448 * 2^k) the byte is the exact smallest
+    power of two >= max/448; it is the floor rule's byte, plus one when the max's mantissa exceeds
+    1.75 (448 = 1.75 * 2^8).  At the edge it is the exact byte or one less."""
+    rng = np.random.default_rng(11)
+    amax = (rng.random(4000) * 2 + 0.5) * np.exp2(rng.integers(-60, 60, 4000).astype(np.float64))
+    amax = amax.astype(np.float32).astype(np.float64)
+    up = oracle.mx_scale_bytes_roundup(amax).astype(int)
+    fl = oracle.mx_scale_bytes(amax).astype(int)
+    F = np.floor(np.log2(amax))
+    m = amax / np.exp2(F)
+    for a, u, f, mm in zip(amax, up, fl, m):
+        exact = _exact_roundup_byte(a)
+        if abs(mm - 1.75) > 2.0 ** -20:
+            assert u == exact, (a, u, exact)
+            assert u == f + (1 if mm > 1.75 else 0), (a, u, f)
+        else:
+            assert u in (exact, exact - 1)
+    # the edge itself: one f32 ulp either side of 448 * 2^k
+    for k in (-3, 0, 5):
+        base = np.float32(448.0 * 2.0 ** k)
+        for a in (np.nextafter(base, np.float32(0)), base, np.nextafter(base, np.float32(np.inf))):
+            u = int(oracle.mx_scale_bytes_roundup([float(a)])[0])
+            assert u in (_exact_roundup_byte(float(a)), _exact_roundup_byte(float(a)) - 1)
+
+
+def test_roundup_quantiser_never_clips_beyond_rounding():
+    """With the round-up rule the block max lands in (224, 448] units (448 (1 + 2^-22) at the f32
+    edge, saturated to 448), so no element is clipped; codes round as under the default rule."""
+    rng = np.random.default_rng(12)
+    x = (rng.standard_normal((64, 256)) * np.exp2(rng.integers(-30, 30, (64, 1)))).astype(np.float32)
+    x[rng.random(x.shape) < 0.02] *= 64
+    codes, scales = oracle.mx_quantize(x, rule="roundup")
+    unit = np.repeat(np.exp2(scales.astype(np.float64) - 127), 32, axis=1)
+    y = x.astype(np.float64) / unit
+    bmax = np.abs(y).reshape(64, 8, 32).max(axis=2)
+    assert np.all(bmax > 224) and np.all(bmax <= 448 * (1 + 2.0 ** -22))
+    # the codes are the default rule's rounding of x / scale
+    for r in range(0, 64, 9):
+        for b in range(8):
+            blk = y[r, 32 * b:32 * b + 32]
+            for i in range(0, 32, 5):
+                want = _exhaustive_nearest(blk[i]) if abs(blk[i]) <= 448 else (0x7E | (0x80 if blk[i] < 0 else 0))
+                assert codes[r, 32 * b + i] == want
+    with pytest.raises(ValueError):
+        oracle.mx_quantize(x, rule="nearest")
