@@ -43,9 +43,12 @@ KERNEL_SOURCES = {
     "quantize": ["mx_quantize.hip", "common.hpp"],
     "quantize_t": ["mx_quantize.hip", "common.hpp"],
     "grouped": ["grouped_mxfp8.hip", "mx_gemm_core.hpp", "common.hpp"],
+    "forward": ["grouped_mxfp8.hip", "mx_gemm_core.hpp", "common.hpp"],
+    "a8w4": ["grouped_mxfp8.hip", "mx_gemm_core.hpp", "common.hpp"],
 }
 KERNEL_NAMES = {"wgrad": "wgrad_mxfp8_kernel", "dgrad": "dgrad_f32_kernel", "quantize": "mx_quantize_kernel",
-                "quantize_t": "mx_quantize_t_kernel", "grouped": "grouped_mxfp8_kernel"}
+                "quantize_t": "mx_quantize_t_kernel", "grouped": "grouped_mxfp8_kernel",
+                "forward": "grouped_mxfp8_kernel", "a8w4": "grouped_mxfp8_kernel"}
 
 
 def source_digest(pass_name: str) -> str:
@@ -255,6 +258,59 @@ def bench_grouped(torch, mg, idx, steps, warmup, cpu_baseline, fast=False):
     return line
 
 
+def bench_forward(torch, mg, idx, steps, warmup, cpu_baseline, fast=False, fp4=False):
+    """The MoE forward y = x W_e^T on the expert-grouped GEMM: A = MX(x) along K, B[e] = MXFP8(W_e)
+    or, with fp4, MXFP4(W_e) (a8w4); operands quantised on the GPU."""
+    inp = wl.make_forward_inputs(idx)
+    d = torch.device("cuda:0")
+    x = torch.from_numpy(inp["x"]).to(d)
+    W = torch.from_numpy(inp["W"]).to(d)
+    off = torch.from_numpy(inp["off"]).to(d)
+    M, K = x.shape
+    E, N, _ = W.shape
+    qa, sa = mg.mx_quantize(x)
+    if fp4:
+        qb, sb = mg.mx4_quantize(W.view(E * N, K))
+        qb, sb = qb.view(E, N, K // 2), sb.view(E, N, K // 32)
+    else:
+        qb, sb = mg.mx_quantize(W.view(E * N, K))
+        qb, sb = qb.view(E, N, K), sb.view(E, N, K // 32)
+    torch.cuda.synchronize()
+    del x, W
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=d)
+    ms = time_steps(torch, lambda: mg.grouped_mxfp8(qa, qb, sa, sb, off, out=out, fast=fast, b_fp4=fp4),
+                    steps, warmup)
+    flop = 2.0 * M * N * K
+    tf = flop / (ms * 1e-3) / 1e12
+    wbytes = N * K // 2 if fp4 else N * K
+    nonempty = int(np.count_nonzero(np.diff(inp["off"])))
+    nbytes = M * K + M * K // 32 + nonempty * (wbytes + N * K // 32) + 2 * M * N
+    name = "a8w4" if fp4 else "forward"
+    line = {"metric": f"TFLOP/s, MoE forward y = x W_e^T ({'MXFP4' if fp4 else 'MXFP8'} weights) on workload {idx} (1 GPU)",
+            "value": round(tf, 2), "unit": "TFLOP/s", "pct_of_fp8_peak": round(100 * tf / PEAK_FP8_TFLOPS, 2),
+            "ms_per_step": round(ms, 4),
+            "dtype": ("fp8e4m3*fp4e2m1" if fp4 else "fp8e4m3*fp8e4m3") + "->f32 acc, bf16 out",
+            "mode": "single block-scaled MFMA pass" if fast else "two block-scaled MFMA passes (A codes >= 128 / the rest)",
+            "config": {"workload": wl.WORKLOADS[idx].name, "E": E, "M": M, "K_in": K, "N_out": N},
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_FP8_TFLOPS, 4),
+                         "traffic": None if fast else read_traffic(name, idx),
+                         "algorithmic_bytes": int(nbytes), "algorithmic_flop": flop}}
+    if cpu_baseline:
+        import oracle
+        rows = int(inp["off"][E // 8])                            # the tokens of the first E/8 experts
+        qa_h, sa_h = qa[:rows].cpu().numpy(), sa[:rows].cpu().numpy()
+        qb_h, sb_h = qb[: E // 8].cpu().numpy(), sb[: E // 8].cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.grouped_gemm(qa_h, sa_h, qb_h, sb_h, inp["off"][: E // 8 + 1], b_format="e2m1" if fp4 else "e4m3")
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": round(2.0 * rows * N * K / dt / 1e12, 4), "unit": "TFLOP/s",
+                                "cores": blas_threads(), "kind": "oracle", "seconds": round(dt, 2),
+                                "cpu": cpu_info(),
+                                "sample": f"the {rows} token rows of experts 0..{E // 8 - 1} (oracle.grouped_gemm, fp64)"}
+    return line
+
+
 def bench_quantize(torch, mg, idx, steps, warmup, cpu_baseline):
     inp = wl.make_wgrad_inputs(idx)
     d = torch.device("cuda:0")
@@ -331,7 +387,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--pass", dest="pass_name", choices=["wgrad", "grouped", "dgrad", "quantize", "quantize_t", "copy"], default="wgrad")
+    ap.add_argument("--pass", dest="pass_name", choices=["wgrad", "grouped", "forward", "a8w4", "dgrad", "quantize", "quantize_t", "copy"], default="wgrad")
     ap.add_argument("--workload", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fast", action="store_true", help="wgrad: the single-pass entry point")
@@ -348,11 +404,14 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
 
-    idx = args.workload or {"wgrad": 4, "grouped": 5, "dgrad": 5, "quantize": 4, "quantize_t": 4,
-                            "copy": 0}[args.pass_name]
-    fn = {"wgrad": bench_wgrad, "grouped": bench_grouped, "dgrad": bench_dgrad, "quantize": bench_quantize,
-          "quantize_t": bench_quantize_t, "copy": bench_copy}[args.pass_name]
-    kw = {"fast": True} if (args.fast and args.pass_name in ("wgrad", "grouped")) else {}
+    idx = args.workload or {"wgrad": 4, "grouped": 5, "forward": 5, "a8w4": 5, "dgrad": 5, "quantize": 4,
+                            "quantize_t": 4, "copy": 0}[args.pass_name]
+    fn = {"wgrad": bench_wgrad, "grouped": bench_grouped, "forward": bench_forward, "a8w4": bench_forward,
+          "dgrad": bench_dgrad, "quantize": bench_quantize, "quantize_t": bench_quantize_t,
+          "copy": bench_copy}[args.pass_name]
+    kw = {"fast": True} if (args.fast and args.pass_name in ("wgrad", "grouped", "forward", "a8w4")) else {}
+    if args.pass_name == "a8w4":
+        kw["fp4"] = True
     line = fn(torch, mg, idx, args.steps, args.warmup, not args.no_cpu_baseline, **kw)
     line.update({"n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
                  "higher_is_better": True, "scaling": "weak", "vs_baseline": None,

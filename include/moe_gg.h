@@ -173,6 +173,37 @@ MOE_GG_API int moe_gg_grouped_mxfp8_fast(const uint8_t *A, const uint8_t *B, uin
                                          hipStream_t stream);
 
 /*
+ * Expert-grouped GEMM with MXFP4 weights (a8w4): the same as
+ * moe_gg_grouped_mxfp8 with B[e] holding E2M1 codes.
+ *
+ * Source: the decode page's a8w4 MoE stages and mfma_f4f8 (fp4 weights with
+ * one E8M0 scale per 32 along k, times MXFP8 activations, on the f8f6f4
+ * scaled MFMA with format 4 for the fp4 operand); the token bucketing as for
+ * moe_gg_grouped_mxfp8.
+ *
+ *   A        E4M3 bytes [M][K]        (token rows)
+ *   B        E2M1 codes [E][N][K/2]   two per byte along K, element 2i in the
+ *            low nibble (moe_gg_mx4_quantize's layout)
+ *   C        bf16 bits  [M][N], every element written
+ *   scale_A  E8M0 [M][K/32]; scale_B  E8M0 [E][N][K/32]
+ *   expert_off int32 [E+1] as for moe_gg_grouped_mxfp8
+ *
+ *   C[m][j] = bf16_rne( sum over c of deq(A)[m][c] deq4(B[e(m)])[j][c] )
+ *
+ * The MoE forward y = x W_e^T with A = MX(x) along K and B[e] = MXFP4(W_e)
+ * along K.  Shapes and status codes as moe_gg_grouped_mxfp8; the default
+ * entry point splits A's codes into two MFMA passes, the _fast one makes one.
+ */
+MOE_GG_API int moe_gg_grouped_a8w4(const uint8_t *A, const uint8_t *B, uint16_t *C,
+                                   const uint8_t *scale_A, const uint8_t *scale_B,
+                                   const int32_t *expert_off, int M, int N, int K, int E,
+                                   hipStream_t stream);
+MOE_GG_API int moe_gg_grouped_a8w4_fast(const uint8_t *A, const uint8_t *B, uint16_t *C,
+                                        const uint8_t *scale_A, const uint8_t *scale_B,
+                                        const int32_t *expert_off, int M, int N, int K, int E,
+                                        hipStream_t stream);
+
+/*
  * MX quantiser: f32 [R][L] -> E4M3 codes [R][L] + E8M0 scales [R][L/32],
  * blocks of 32 consecutive elements along L (aligned to the start of a row).
  *
@@ -225,6 +256,24 @@ MOE_GG_API int moe_gg_mx_quantize_roundup(const float *X, uint8_t *Q, uint8_t *S
                                           hipStream_t stream);
 MOE_GG_API int moe_gg_mx_quantize_t_roundup(const float *X, uint8_t *Q, uint8_t *S, int R, int L,
                                             hipStream_t stream);
+
+/*
+ * MXFP4 quantiser: f32 [R][L] -> E2M1 codes [R][L/2] (two per byte, element
+ * 2i in the low nibble) + E8M0 scales [R][L/32], blocks of 32 along L.
+ *
+ * Source: the decode page's fp4 weights (format 4 of the f8f6f4 MFMA, one
+ * E8M0 scale per 32 along k); the page does not print their quantiser, so
+ * this is the MX rule with E2M1's largest exponent, 2, in place of E4M3's 8:
+ *
+ *   s = clamp(floor(log2(max |X[r][32j..32j+31]|)) - 2 + 127, 1, 254), s = 1 for a zero block
+ *   code = e2m1_rne_saturate(X * 2^(127 - s)): nearest of 0, 0.5, 1, 1.5, 2,
+ *          3, 4, 6, ties to the even code, +-6 beyond; sign bit kept
+ *
+ * Inputs must be finite.  Shapes: R >= 1, L >= 32, L % 32 == 0 (EINVAL
+ * otherwise).
+ */
+MOE_GG_API int moe_gg_mx4_quantize(const float *X, uint8_t *Q, uint8_t *S, int R, int L,
+                                   hipStream_t stream);
 
 /*
  * Row -> expert map, the integer step of the data gradient, exposed so that

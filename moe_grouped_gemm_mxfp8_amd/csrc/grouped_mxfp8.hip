@@ -28,6 +28,11 @@
 //    expert passes as one stream, and waves 4-7 issue all stage loads.
 //  * Rows past M read as zero (buffer-descriptor range) and their stores are
 //    dropped the same way, so M needs no padding.
+//  * a8w4 (the decode page's mfma_f4f8: fp4 weights times MXFP8 activations):
+//    B[e] may hold E2M1 codes, two per byte along the contraction, with the
+//    same E8M0 scales; the weight tile is then 16 KB per step (MFMA format 4
+//    for the x-role), loaded by four stage loads per loading wave instead of
+//    eight.
 #include "common.hpp"
 #include "mx_gemm_core.hpp"
 #include "../../include/moe_gg.h"
@@ -39,7 +44,6 @@ using namespace mxgemm;
 
 constexpr int NWAVE = 8;
 constexpr int NTHREAD = NWAVE * 64;
-constexpr int LOADS_PER_STEP = 18;            // stage loads a loading wave issues per step
 
 constexpr int MAX_E = 2048;                   // experts (LDS tables of E + 1 entries)
 constexpr int SCAN_PER = (MAX_E + 1 + NTHREAD - 1) / NTHREAD;   // table entries per thread in the scans
@@ -63,7 +67,7 @@ struct Tile {
   int kind, e, jt, m0, rows;
 };
 
-template <bool SPLIT>
+template <bool SPLIT, bool XFP4>
 __global__ __launch_bounds__(NTHREAD, 1) void grouped_mxfp8_kernel(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, uint16_t *__restrict__ C,
     const uint8_t *__restrict__ SA, const uint8_t *__restrict__ SB,
@@ -161,7 +165,11 @@ __global__ __launch_bounds__(NTHREAD, 1) void grouped_mxfp8_kernel(
   // ---- per-lane constants -------------------------------------------------
   const uint32_t smem_base = lds_addr(smem);
   const uint32_t Kb = static_cast<uint32_t>(K);
+  const uint32_t Kx = XFP4 ? Kb / 2 : Kb;  // bytes per weight row
   const uint32_t scale_row = Kb / 32;      // bytes per scale row
+  // stage loads a loading wave issues per step: 8 (E4M3) or 4 (fp4) for the
+  // weight tile, 8 for the token tile, 2 scale loads
+  constexpr int LOADS_PER_STEP = (XFP4 ? 4 : 8) + 8 + 2;
   // Stage loads by waves 4-7: wave 4 + w4 fills blocks 8w4..8w4+7 of both
   // operand tiles (block 8G + q holds rows 64G + 8j + q at slot j; lane L ->
   // slot L/8, bytes 16(L%8)..16(L%8)+15 of the row's step) and the scale
@@ -175,13 +183,20 @@ __global__ __launch_bounds__(NTHREAD, 1) void grouped_mxfp8_kernel(
     voff_t[i] = static_cast<uint32_t>(r) * Kb + static_cast<uint32_t>(lane & 7) * 16u;
   }
   const uint32_t voff_s = static_cast<uint32_t>(w4 * 64 + lane) * scale_row;
+  // fp4 weight tile: wave 4 + w4 fills blocks 4w4..4w4+3 (block 4G + q holds
+  // rows 64G + 4j + q at slot j; lane L -> slot L/4, bytes 16(L%4)..+15)
+  uint32_t voff_x4[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    voff_x4[i] = static_cast<uint32_t>(64 * w4 + 4 * (lane >> 2) + i) * Kx + static_cast<uint32_t>(lane & 3) * 16u;
 
   // MFMA operand addressing
   const int wk = wave >> 2, wn = wave & 3;
   const int g = lane >> 5, l32 = lane & 31;
   uint32_t xrow[4], grow[2];
 #pragma unroll
-  for (int a = 0; a < 4; ++a) xrow[a] = ST_X + tile_row(wk * 128 + a * 32 + l32);
+  for (int a = 0; a < 4; ++a)
+    xrow[a] = ST_X + (XFP4 ? tile_row4(wk * 128 + a * 32 + l32) : tile_row(wk * 128 + a * 32 + l32));
 #pragma unroll
   for (int bb = 0; bb < 2; ++bb) grow[bb] = ST_G + tile_row(wn * 64 + bb * 32 + l32);
   uint32_t chunk_off[2][2];   // [half][piece] -> 16-byte chunk offset within the row
@@ -210,12 +225,18 @@ __global__ __launch_bounds__(NTHREAD, 1) void grouped_mxfp8_kernel(
     const uint32_t cpos = static_cast<uint32_t>(ld_s * TT);
     const size_t wrow = static_cast<size_t>(ld_t.e) * N + static_cast<size_t>(ld_t.jt) * TK;   // first weight row
     const uint32_t rows = static_cast<uint32_t>(ld_t.rows);
-    const v4i srd_x = make_srd(B + wrow * K, TK * Kb);
+    const v4i srd_x = make_srd(B + wrow * Kx, TK * Kx);
     const v4i srd_g = make_srd(A + static_cast<size_t>(ld_t.m0) * K, rows * Kb);
     const uint32_t base = smem_base + buf * STAGE_BYTES;
+    if constexpr (XFP4) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      dma_b128(srd_x, voff_t[i], cpos, __builtin_amdgcn_readfirstlane(base + ST_X + (w4 * 8 + i) * BLK));
+      for (int i = 0; i < 4; ++i)
+        dma_b128(srd_x, voff_x4[i], cpos / 2, __builtin_amdgcn_readfirstlane(base + ST_X + (w4 * 4 + i) * BLK4));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        dma_b128(srd_x, voff_t[i], cpos, __builtin_amdgcn_readfirstlane(base + ST_X + (w4 * 8 + i) * BLK));
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       dma_b128(srd_g, voff_t[i], cpos, __builtin_amdgcn_readfirstlane(base + ST_G + (w4 * 8 + i) * BLK));
@@ -227,12 +248,15 @@ __global__ __launch_bounds__(NTHREAD, 1) void grouped_mxfp8_kernel(
   };
   // wait until the loads of the step in buffer b have landed: every vector
   // memory instruction issued after them may still be in flight
+  // (the counts that occur: a step's loads, a tile's stores, both, and a
+  // zero tile's stores on top; any smaller count is also correct)
   auto wait_step = [&](int bf) __attribute__((always_inline)) {
+    constexpr int L = LOADS_PER_STEP, S = STORES_PER_TILE;
     const int younger = ops - mark[bf];
-    if (younger >= 50) wait_vmcnt<50>();
-    else if (younger >= 34) wait_vmcnt<34>();
-    else if (younger >= 18) wait_vmcnt<18>();
-    else if (younger >= 16) wait_vmcnt<16>();
+    if (younger >= L + 2 * S) wait_vmcnt<L + 2 * S>();
+    else if (younger >= L + S) wait_vmcnt<L + S>();
+    else if (younger >= (L > S ? L : S)) wait_vmcnt<(L > S ? L : S)>();
+    else if (younger >= (L > S ? S : L)) wait_vmcnt<(L > S ? S : L)>();
     else if (younger >= 8) wait_vmcnt<8>();
     else wait_vmcnt<0>();
   };
@@ -275,7 +299,7 @@ __global__ __launch_bounds__(NTHREAD, 1) void grouped_mxfp8_kernel(
         advance();
       }
       const uint8_t *st = smem + buf * STAGE_BYTES;
-      compute_step<SPLIT>(st, acc, xrow, grow, chunk_off, wk, wn, l32, g, 0, TT, 0, TN);
+      compute_step<SPLIT, XFP4>(st, acc, xrow, grow, chunk_off, wk, wn, l32, g, 0, TT, 0, TN);
       buf ^= 1;
     }
     // ---- epilogue: C[m0 + m][j0 + j] for the tile's rows; the descriptor
@@ -286,7 +310,7 @@ __global__ __launch_bounds__(NTHREAD, 1) void grouped_mxfp8_kernel(
   wait_vmcnt<0>();
 }
 
-int launch_grouped(bool split, const uint8_t *A, const uint8_t *B, uint16_t *C, const uint8_t *scale_A,
+int launch_grouped(bool split, bool xfp4, const uint8_t *A, const uint8_t *B, uint16_t *C, const uint8_t *scale_A,
                    const uint8_t *scale_B, const int32_t *expert_off, int M, int N, int K, int E,
                    hipStream_t stream) {
   if (!A || !B || !C || !scale_A || !scale_B || !expert_off) return MOE_GG_EINVAL;
@@ -305,12 +329,14 @@ int launch_grouped(bool split, const uint8_t *A, const uint8_t *B, uint16_t *C, 
   const int64_t total = (static_cast<int64_t>((M + TN - 1) / TN) + E + 2) * (N / TK);
   if (total > 0x7FFFFFFF) return MOE_GG_EUNSUPPORTED;
   const int grid = static_cast<int>(total < cus ? total : cus);
-  if (split)
-    hipLaunchKernelGGL(grouped_mxfp8_kernel<true>, dim3(grid), dim3(NTHREAD), 0, stream, A, B, C, scale_A,
-                       scale_B, expert_off, M, N, K, E);
-  else
-    hipLaunchKernelGGL(grouped_mxfp8_kernel<false>, dim3(grid), dim3(NTHREAD), 0, stream, A, B, C, scale_A,
-                       scale_B, expert_off, M, N, K, E);
+#define MOE_GG_LAUNCH(S, X)                                                                              \
+  hipLaunchKernelGGL((grouped_mxfp8_kernel<S, X>), dim3(grid), dim3(NTHREAD), 0, stream, A, B, C, scale_A, \
+                     scale_B, expert_off, M, N, K, E)
+  if (split && xfp4) MOE_GG_LAUNCH(true, true);
+  else if (split) MOE_GG_LAUNCH(true, false);
+  else if (xfp4) MOE_GG_LAUNCH(false, true);
+  else MOE_GG_LAUNCH(false, false);
+#undef MOE_GG_LAUNCH
   return hipGetLastError() == hipSuccess ? MOE_GG_OK : MOE_GG_ELAUNCH;
 }
 
@@ -321,12 +347,26 @@ extern "C" MOE_GG_API int moe_gg_grouped_mxfp8(const uint8_t *A, const uint8_t *
                                                const uint8_t *scale_A, const uint8_t *scale_B,
                                                const int32_t *expert_off, int M, int N, int K, int E,
                                                hipStream_t stream) {
-  return moe_gg::launch_grouped(true, A, B, C, scale_A, scale_B, expert_off, M, N, K, E, stream);
+  return moe_gg::launch_grouped(true, false, A, B, C, scale_A, scale_B, expert_off, M, N, K, E, stream);
 }
 
 extern "C" MOE_GG_API int moe_gg_grouped_mxfp8_fast(const uint8_t *A, const uint8_t *B, uint16_t *C,
                                                     const uint8_t *scale_A, const uint8_t *scale_B,
                                                     const int32_t *expert_off, int M, int N, int K, int E,
                                                     hipStream_t stream) {
-  return moe_gg::launch_grouped(false, A, B, C, scale_A, scale_B, expert_off, M, N, K, E, stream);
+  return moe_gg::launch_grouped(false, false, A, B, C, scale_A, scale_B, expert_off, M, N, K, E, stream);
+}
+
+extern "C" MOE_GG_API int moe_gg_grouped_a8w4(const uint8_t *A, const uint8_t *B, uint16_t *C,
+                                              const uint8_t *scale_A, const uint8_t *scale_B,
+                                              const int32_t *expert_off, int M, int N, int K, int E,
+                                              hipStream_t stream) {
+  return moe_gg::launch_grouped(true, true, A, B, C, scale_A, scale_B, expert_off, M, N, K, E, stream);
+}
+
+extern "C" MOE_GG_API int moe_gg_grouped_a8w4_fast(const uint8_t *A, const uint8_t *B, uint16_t *C,
+                                                   const uint8_t *scale_A, const uint8_t *scale_B,
+                                                   const int32_t *expert_off, int M, int N, int K, int E,
+                                                   hipStream_t stream) {
+  return moe_gg::launch_grouped(false, true, A, B, C, scale_A, scale_B, expert_off, M, N, K, E, stream);
 }

@@ -9,6 +9,15 @@
 // one stage-load instruction fills a block, eight lanes per row reading the
 // row's 128 bytes in order, and the padding puts the 16 rows an MFMA operand
 // read touches at once on 16 distinct bank groups.
+//
+// The x-role tile may instead hold E2M1 (fp4) codes, two per byte (MFMA
+// format 4): 256 rows x 64 bytes per step, 16 blocks of 16 rows x 64 bytes,
+// each padded by 16 bytes.  Row r sits in block 4(r/64) + r%4 at slot
+// (r%64)/4, so a stage load fills a block with four lanes per row reading
+// its 64 bytes in order, and the 16 rows an operand read touches at once
+// (r%4 and (r/4)%4 all different) fall on 16 distinct bank groups.  A lane's
+// fp4 operand of a 64-deep half is 16 bytes: the 32 codes of its 32-element
+// block (lane group g = block g of the half), low nibble first.
 #pragma once
 
 #include "common.hpp"
@@ -32,6 +41,14 @@ static_assert(128 * 512 <= STAGE_BYTES, "the epilogue stages 128 rows of 512 byt
 // LDS byte offset of row r (0..255) inside an operand tile.
 __device__ __forceinline__ uint32_t tile_row(int r) {
   return static_cast<uint32_t>(((r >> 6) * 8 + (r & 7)) * BLK + ((r & 63) >> 3) * TT);
+}
+
+// The same for an fp4 x-role tile (64 bytes per row and step).
+constexpr int TT4 = TT / 2;                   // bytes of an fp4 row per step
+constexpr int BLK4 = 16 * TT4 + 16;           // 1040: 16 rows of 64 bytes + padding
+static_assert(16 * BLK4 <= TILE_BYTES, "an fp4 x-role tile fits the x-role area");
+__device__ __forceinline__ uint32_t tile_row4(int r) {
+  return static_cast<uint32_t>(((r >> 6) * 4 + (r & 3)) * BLK4 + ((r & 63) >> 2) * TT4);
 }
 
 // Byte mask of the E4M3 codes in a dword whose magnitude is >= 128
@@ -73,7 +90,7 @@ __device__ __forceinline__ void mask_tokens(v8i &frag, int h, int g, int rlo, in
 // g-role fragments first (both bounds step- and tile-relative).  The fragments of both 64-token halves are
 // read from LDS up front and the MFMAs of the first half are interleaved
 // with the reads of the second, so only the first reads' latency is exposed.
-template <bool SPLIT>
+template <bool SPLIT, bool XFP4 = false>
 __device__ __forceinline__ void compute_step(const uint8_t *st, v16f (&acc)[4][2], const uint32_t (&xrow)[4],
                                              const uint32_t (&grow)[2], const uint32_t (&chunk_off)[2][2],
                                              int wk, int wn, int l32, int g, int rlo, int rhi, int row_lo,
@@ -90,13 +107,24 @@ __device__ __forceinline__ void compute_step(const uint8_t *st, v16f (&acc)[4][2
     const v4i hi = *reinterpret_cast<const v4i *>(st + row + chunk_off[h][1]);
     return (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   };
+  // x-role fragment of half h: E4M3 as above, or the 16 bytes of fp4 codes of
+  // this lane's 32-element block (the MFMA reads the low four dwords)
+  auto xfrag = [&](uint32_t row, int h) {
+    if constexpr (XFP4) {
+      const v4i v = *reinterpret_cast<const v4i *>(st + row + (2 * h + g) * 16);
+      return (v8i){v[0], v[1], v[2], v[3], 0, 0, 0, 0};
+    } else {
+      return frag(row, h);
+    }
+  };
+  constexpr int XFMT = XFP4 ? 4 : 0;           // MFMA A-operand format: E2M1 or E4M3
   auto mm = [&](int a, int b, const v8i &x, const v8i &gop, int h) {
     if (h == 0)
       acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-          x, gop, acc[a][b], 0, 0, 0, static_cast<int>(sx[a]), 0, static_cast<int>(sg[b]));
+          x, gop, acc[a][b], XFMT, 0, 0, static_cast<int>(sx[a]), 0, static_cast<int>(sg[b]));
     else
       acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-          x, gop, acc[a][b], 0, 0, 2, static_cast<int>(sx[a]), 2, static_cast<int>(sg[b]));
+          x, gop, acc[a][b], XFMT, 0, 2, static_cast<int>(sx[a]), 2, static_cast<int>(sg[b]));
   };
   // first half: g fragments and x fragments; second half: g fragments early,
   // each x fragment as soon as the first half's fragment of the same rows is done
@@ -104,7 +132,7 @@ __device__ __forceinline__ void compute_step(const uint8_t *st, v16f (&acc)[4][2
 #pragma unroll
   for (int b = 0; b < 2; ++b) g0[b] = frag(grow[b], 0);
 #pragma unroll
-  for (int a = 0; a < 4; ++a) x[a] = frag(xrow[a], 0);
+  for (int a = 0; a < 4; ++a) x[a] = xfrag(xrow[a], 0);
 #pragma unroll
   for (int b = 0; b < 2; ++b) g1[b] = frag(grow[b], 1);
   if (rlo > 0 || rhi < TT) {
@@ -152,7 +180,7 @@ __device__ __forceinline__ void compute_step(const uint8_t *st, v16f (&acc)[4][2
       for (int a = 0; a < 4; ++a) {
         mm(a, 0, x[a], gl[0], h);
         mm(a, 1, x[a], gl[1], h);
-        if (h == 0) x[a] = frag(xrow[a], 1);
+        if (h == 0) x[a] = xfrag(xrow[a], 1);
       }
     }
   } else {
@@ -160,7 +188,7 @@ __device__ __forceinline__ void compute_step(const uint8_t *st, v16f (&acc)[4][2
     for (int a = 0; a < 4; ++a) {
       mm(a, 0, x[a], g0[0], 0);
       mm(a, 1, x[a], g0[1], 0);
-      x[a] = frag(xrow[a], 1);
+      x[a] = xfrag(xrow[a], 1);
     }
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
@@ -168,11 +196,12 @@ __device__ __forceinline__ void compute_step(const uint8_t *st, v16f (&acc)[4][2
       mm(a, 1, x[a], g1[1], 1);
     }
     // scales and first-half reads, then MFMAs with the second half's x reads between
-    __builtin_amdgcn_sched_group_barrier(0x100, 22, 0);
+    // (an fp4 x fragment is one 16-byte read instead of two)
+    __builtin_amdgcn_sched_group_barrier(0x100, XFP4 ? 18 : 22, 0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, XFP4 ? 1 : 2, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
   }

@@ -35,6 +35,15 @@
 // feature-major, then one thread per (feature, 32-token block) computes the
 // block's scale and writes its 32 codes as two 16-byte stores, four threads
 // covering a feature row's 128 bytes.
+//
+// mx4_quantize: MXFP4 (E2M1 codes, two per byte, element 2i in the low
+// nibble; the operand order of the gfx950 MFMA's format 4).  Scale
+// 2^(floor(log2(block max)) - 2), 2 being E2M1's largest exponent as 8 is
+// E4M3's, the byte clamped to [1, 254] (1 for a zero block).  Codes: nearest
+// E2M1 value, ties to the even code, saturating at +-6, sign kept; written
+// out as seven threshold comparisons on |y| (strict at the ties that round
+// down to an even code, inclusive at those that round up to one), which is
+// exact.  Same streaming layout as mx_quantize, 2 bytes of codes per lane.
 #include "common.hpp"
 #include "../../include/moe_gg.h"
 
@@ -93,6 +102,51 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(const float *__restric
       const uint32_t word = e4m3x4(v, sb);
       if (live) {
         __builtin_nontemporal_store(word, reinterpret_cast<uint32_t *>(Q + i0));
+        if ((lane & 7) == 0) S[i0 >> 5] = static_cast<uint8_t>(sb);
+      }
+    }
+  }
+}
+
+// E2M1 code of y (4 bits): |y| against the midpoints 0.25, 0.75, 1.25, 1.75,
+// 2.5, 3.5 and 5 of the magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+__device__ __forceinline__ uint32_t e2m1_code(float y) {
+  const float a = __builtin_fabsf(y);
+  const uint32_t c = (a > 0.25f ? 1u : 0u) + (a >= 0.75f ? 1u : 0u) + (a > 1.25f ? 1u : 0u) +
+                     (a >= 1.75f ? 1u : 0u) + (a > 2.5f ? 1u : 0u) + (a >= 3.5f ? 1u : 0u) +
+                     (a > 5.0f ? 1u : 0u);
+  return c | ((__float_as_uint(y) >> 28) & 8u);
+}
+
+__global__ __launch_bounds__(256) void mx4_quantize_kernel(const float *__restrict__ X, uint8_t *__restrict__ Q,
+                                                           uint8_t *__restrict__ S, int64_t total) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave_global = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
+  const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 6;
+  for (int64_t base = wave_global * 512; base < total; base += nwaves * 512) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int64_t i0 = base + half * 256 + 4 * lane;   // this lane's 4 elements
+      const bool live = i0 < total;                       // whole 32-blocks are live or not
+      v4f v = live ? __builtin_nontemporal_load(reinterpret_cast<const v4f *>(X + i0)) : (v4f){0.f, 0.f, 0.f, 0.f};
+      uint32_t m = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m = max(m, __float_as_uint(v[i]) & 0x7FFFFFFFu);
+      m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 1)));
+      m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 2)));
+      m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 4)));
+      uint32_t sb = 1u;
+      if (m != 0) {
+        const int s = floor_log2_bits(m) - 2 + 127;
+        sb = static_cast<uint32_t>(s < 1 ? 1 : (s > 254 ? 254 : s));
+      }
+      // 2^(127 - sb) with sb <= 252 for a finite max: a normal f32
+      const float f = __uint_as_float((254u - sb) << 23);
+      uint32_t codes = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) codes |= e2m1_code(v[i] * f) << (4 * i);
+      if (live) {
+        __builtin_nontemporal_store(static_cast<uint16_t>(codes), reinterpret_cast<uint16_t *>(Q + (i0 >> 1)));
         if ((lane & 7) == 0) S[i0 >> 5] = static_cast<uint8_t>(sb);
       }
     }
@@ -183,6 +237,21 @@ int launch_quantize(bool roundup, const float *X, uint8_t *Q, uint8_t *S, int R,
   return hipGetLastError() == hipSuccess ? MOE_GG_OK : MOE_GG_ELAUNCH;
 }
 
+int launch_quantize4(const float *X, uint8_t *Q, uint8_t *S, int R, int L, hipStream_t stream) {
+  if (!X || !Q || !S || R <= 0 || L < 32 || L % 32) return MOE_GG_EINVAL;
+  const int64_t total = static_cast<int64_t>(R) * L;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_GG_ELAUNCH;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return MOE_GG_ELAUNCH;
+  const int64_t waves_needed = (total + 511) / 512;
+  int64_t blocks = (waves_needed + 3) / 4;
+  const int64_t cap = static_cast<int64_t>(cus) * 16;
+  if (blocks > cap) blocks = cap;
+  hipLaunchKernelGGL(mx4_quantize_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, X, Q, S, total);
+  return hipGetLastError() == hipSuccess ? MOE_GG_OK : MOE_GG_ELAUNCH;
+}
+
 }  // namespace
 }  // namespace moe_gg
 
@@ -204,4 +273,9 @@ extern "C" MOE_GG_API int moe_gg_mx_quantize(const float *X, uint8_t *Q, uint8_t
 extern "C" MOE_GG_API int moe_gg_mx_quantize_roundup(const float *X, uint8_t *Q, uint8_t *S, int R, int L,
                                                      hipStream_t stream) {
   return moe_gg::launch_quantize(true, X, Q, S, R, L, stream);
+}
+
+extern "C" MOE_GG_API int moe_gg_mx4_quantize(const float *X, uint8_t *Q, uint8_t *S, int R, int L,
+                                              hipStream_t stream) {
+  return moe_gg::launch_quantize4(X, Q, S, R, L, stream);
 }

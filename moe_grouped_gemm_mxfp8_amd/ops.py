@@ -5,7 +5,8 @@ import torch
 
 from ._lib import call
 
-__all__ = ["wgrad_mxfp8", "grouped_mxfp8", "dgrad_f32", "mx_quantize", "mx_quantize_t", "row_experts"]
+__all__ = ["wgrad_mxfp8", "grouped_mxfp8", "dgrad_f32", "mx_quantize", "mx_quantize_t", "mx4_quantize",
+           "row_experts"]
 
 
 def _stream() -> int:
@@ -74,17 +75,17 @@ def dgrad_f32(g, w, expert_off, out=None):
     return out
 
 
-def grouped_mxfp8(a, b, scale_a, scale_b, expert_off, out=None, fast=False):
-    """Expert-grouped MXFP8 GEMM: out[m] = deq(a)[m] @ deq(b[e(m)]).T as bf16 [M, N].
+def grouped_mxfp8(a, b, scale_a, scale_b, expert_off, out=None, fast=False, b_fp4=False):
+    """Expert-grouped MX GEMM: out[m] = deq(a)[m] @ deq(b[e(m)]).T as bf16 [M, N].
 
-    a: uint8 E4M3 [M, K]; b: uint8 E4M3 [E, N, K]; scale_a [M, K/32], scale_b [E, N, K/32];
-    expert_off int32 [E+1].
+    a: uint8 E4M3 [M, K]; b: uint8 E4M3 [E, N, K], or with b_fp4 packed E2M1 [E, N, K/2]
+    (moe_gg_grouped_a8w4); scale_a [M, K/32], scale_b [E, N, K/32]; expert_off int32 [E+1].
     """
     for t, name in ((a, "a"), (b, "b"), (scale_a, "scale_a"), (scale_b, "scale_b")):
         _dev(t, name, _U8)
     _dev(expert_off, "expert_off", (torch.int32,))
-    if a.dim() != 2 or b.dim() != 3 or b.shape[2] != a.shape[1]:
-        raise ValueError("a must be [M, K] and b [E, N, K]")
+    if a.dim() != 2 or b.dim() != 3 or b.shape[2] * (2 if b_fp4 else 1) != a.shape[1]:
+        raise ValueError("a must be [M, K] and b [E, N, K] ([E, N, K/2] packed fp4)")
     M, K = a.shape
     E, N, _ = b.shape
     if scale_a.shape != (M, K // 32) or scale_b.shape != (E, N, K // 32):
@@ -96,7 +97,8 @@ def grouped_mxfp8(a, b, scale_a, scale_b, expert_off, out=None, fast=False):
     _dev(out, "out", (torch.bfloat16,))
     if out.shape != (M, N):
         raise ValueError("out must be [M, N]")
-    call("moe_gg_grouped_mxfp8_fast" if fast else "moe_gg_grouped_mxfp8", a.data_ptr(), b.data_ptr(),
+    name = "moe_gg_grouped_a8w4" if b_fp4 else "moe_gg_grouped_mxfp8"
+    call(name + ("_fast" if fast else ""), a.data_ptr(), b.data_ptr(),
          out.data_ptr(), scale_a.data_ptr(), scale_b.data_ptr(), expert_off.data_ptr(), M, N, K, E, _stream())
     return out
 
@@ -126,6 +128,23 @@ def mx_quantize(x, q=None, s=None, rule="floor"):
         s = torch.empty((R, max(L // 32, 1)), dtype=torch.uint8, device=x.device)
     _dev(q, "q", _U8); _dev(s, "s", _U8)
     call("moe_gg_mx_quantize" + suffix, x.data_ptr(), q.data_ptr(), s.data_ptr(), R, L, _stream())
+    return q, s
+
+
+def mx4_quantize(x, q=None, s=None):
+    """MXFP4-quantise f32 x[R, L] along L: (E2M1 codes uint8 [R, L/2], two per byte, E8M0 scales [R, L/32])."""
+    _dev(x, "x", (torch.float32,))
+    if x.dim() != 2:
+        raise ValueError("x must be [R, L]")
+    R, L = x.shape
+    if q is None:
+        q = torch.empty((R, max(L // 2, 1)), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty((R, max(L // 32, 1)), dtype=torch.uint8, device=x.device)
+    _dev(q, "q", _U8); _dev(s, "s", _U8)
+    if q.numel() != R * (L // 2) or s.numel() != R * (L // 32):
+        raise ValueError("q must hold R*L/2 bytes and s R*L/32")
+    call("moe_gg_mx4_quantize", x.data_ptr(), q.data_ptr(), s.data_ptr(), R, L, _stream())
     return q, s
 
 

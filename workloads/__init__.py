@@ -175,3 +175,18 @@ def make_dgrad_inputs(idx: int, seed: int | None = None) -> dict:
     else:
         raise KeyError(idx)
     return {"g": g, "W": W, "off": off}
+
+
+def make_forward_inputs(idx: int, seed: int | None = None) -> dict:
+    """f32 MoE forward inputs ``{"x": [M,K], "W": [E,N,K], "off": [E+1] int32}`` for y = x W_e^T.
+
+    The workload's offsets (same draw as its other passes), then x ~ N(0,1) and
+    W ~ N(0, 0.02), both from the continuing stream.
+    """
+    w = WORKLOADS[idx]
+    assert "dgrad" in w.passes, f"workload {idx} has no expert weights"
+    rng = np.random.default_rng(idx if seed is None else seed)
+    off = make_offsets(idx, rng)
+    x = _normal(rng, (w.M, w.K))
+    W = _normal(rng, (w.E, w.N, w.K), std=0.02)
+    return {"x": x, "W": W, "off": off}
