@@ -5,15 +5,19 @@
 // experts, the overwriting store).
 //
 // Design (gfx950):
-//  * Output tiles of 128 rows x 128 columns, 256 threads = 4 waves as 2 x 2,
-//    each wave a 64 x 64 patch of 2 x 2 v_mfma_f32_32x32x2_f32 accumulators
-//    (f32 products, f32 accumulation: the f32 matrix-core rate).
+//  * Output tiles of 128 rows x 128 columns, 256 threads = 4 waves, wave w
+//    the 32-column strip 32w..32w+31 of the tile as up to four 32 x 32
+//    v_mfma_f32_32x32x2_f32 accumulators, one per 32-row block (f32 products,
+//    f32 accumulation: the f32 matrix-core rate).
 //  * The tile's first and last row give its expert range with a wave-uniform
 //    binary search over the offsets.  A tile inside one expert runs one pass
 //    over n with that expert's W.  A tile whose rows straddle experts runs one
-//    pass per expert present, each pass with the g rows of the other experts
-//    masked to zero, into the same accumulators: every row ends with exactly
-//    its own expert's products.
+//    pass per expert present; a pass multiplies only the 32-row blocks that
+//    hold its expert's rows (the other rows' g loaded as zero) and stores only
+//    those rows at its end, so every row is written once, with exactly its own
+//    expert's products, and a pass over r rows costs ceil(r/32)/4 of a full
+//    one (two passes of a straddling tile together cost 1.25-1.5 passes
+//    instead of 2).
 //  * The contraction runs in chunks of 32 n.  g[128 x 32] and W_e[32 x 128]
 //    are read with 16-byte coalesced loads (g rows and W rows are contiguous
 //    along n and k) into registers, then written to a double-buffered LDS
@@ -45,123 +49,139 @@ __device__ __forceinline__ uint32_t w_lds_off(int n, int col /*float index*/) {
   return LW + n * (BK * 4) + ((col ^ ((n >> 4) << 5)) << 2);
 }
 
+// One expert pass over a tile: rows [lo, hi) of expert e (W_e = We), which lie
+// in the NRB 32-row blocks ib0 .. ib0 + NRB - 1 of the tile; the whole
+// contraction in chunks of 32 n, double-buffered through LDS, then the pass's
+// rows stored.  Every wave runs it (it contains the workgroup's barriers).
+template <int NRB>
+__device__ __forceinline__ void dgrad_pass(const float *__restrict__ G, const float *__restrict__ We,
+                                           float *__restrict__ DX, uint8_t *smem, int M, int N, int K, int r0,
+                                           int k0, int lo, int hi, int ib0, int tid, int wave) {
+  const int lane = tid & 63;
+  const int h = lane >> 5, l32 = lane & 31;
+  // global -> register loader coordinates (4 float4 of g and 4 of W per thread)
+  const int g_row = tid >> 3, g_q = tid & 7;      // rows g_row + 32i, group g_q
+  const int w_n = tid >> 5, w_q = tid & 31;       // n rows w_n + 8i, float4 column w_q
+  const int nchunks = (N + BC - 1) / BC;
+
+  v16f acc[NRB];
+#pragma unroll
+  for (int i = 0; i < NRB; ++i)
+#pragma unroll
+    for (int x = 0; x < 16; ++x) acc[i][x] = 0.f;
+
+  v4f greg[4], wreg[4];
+  auto load_chunk = [&](int c) __attribute__((always_inline)) {
+    const int n0 = c * BC;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = r0 + g_row + 32 * i;
+      const int n = n0 + 4 * g_q;
+      if (r >= lo && r < hi && n < N)
+        greg[i] = *reinterpret_cast<const v4f *>(G + static_cast<size_t>(r) * N + n);
+      else
+        greg[i] = (v4f){0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int n = n0 + w_n + 8 * i;
+      const int k = k0 + 4 * w_q;
+      if (n < N && k < K)
+        wreg[i] = *reinterpret_cast<const v4f *>(We + static_cast<size_t>(n) * K + k);
+      else
+        wreg[i] = (v4f){0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  auto store_chunk = [&](int buf) __attribute__((always_inline)) {
+    uint8_t *st = smem + buf * STAGE;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<v4f *>(st + g_lds_off(g_row + 32 * i, g_q)) = greg[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<v4f *>(st + w_lds_off(w_n + 8 * i, 4 * w_q)) = wreg[i];
+  };
+
+  load_chunk(0);
+  store_chunk(0);
+  barrier();
+  for (int c = 0; c < nchunks; ++c) {
+    const int buf = c & 1;
+    if (c + 1 < nchunks) load_chunk(c + 1);
+    const uint8_t *st = smem + buf * STAGE;
+    // this lane's 16 g values per row block: n = 16h .. 16h+15
+    v4f ga[NRB][4];
+#pragma unroll
+    for (int i = 0; i < NRB; ++i) {
+      const int row = (ib0 + i) * 32 + l32;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        ga[i][q] = *reinterpret_cast<const v4f *>(st + g_lds_off(row, 4 * h + q));
+    }
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const float wb = *reinterpret_cast<const float *>(st + w_lds_off(16 * h + s, wave * 32 + l32));
+#pragma unroll
+      for (int i = 0; i < NRB; ++i)
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(ga[i][s >> 2][s & 3], wb, acc[i], 0, 0, 0);
+    }
+    if (c + 1 < nchunks) store_chunk(buf ^ 1);
+    barrier();
+  }
+
+  // this pass's rows: register x of acc[i] is row (ib0 + i)*32 + 8(x/4) + 4h +
+  // x%4 of the tile, column 32 wave + l32
+  const int col = k0 + wave * 32 + l32;
+  if (col < K) {
+#pragma unroll
+    for (int i = 0; i < NRB; ++i)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const int row = r0 + (ib0 + i) * 32 + 8 * (x >> 2) + 4 * h + (x & 3);
+        if (row >= lo && row < hi) DX[static_cast<size_t>(row) * K + col] = acc[i][x];
+      }
+  }
+}
+
 __global__ __launch_bounds__(NTHREAD, 2) void dgrad_f32_kernel(
     const float *__restrict__ G, const float *__restrict__ W, float *__restrict__ DX,
     const int32_t *__restrict__ off, int M, int N, int K, int E) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wr = wave >> 1, wc = wave & 1;
-  const int h = lane >> 5, l32 = lane & 31;
-
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // column strip 32 wave .. +31
   const int r0 = blockIdx.y * BM;
   const int k0 = blockIdx.x * BK;
   const int r_last = min(r0 + BM, M) - 1;
   const int e_first = __builtin_amdgcn_readfirstlane(expert_of_row(off, E, r0));
   const int e_last = __builtin_amdgcn_readfirstlane(expert_of_row(off, E, r_last));
 
-  // global -> register loader coordinates (4 float4 of g and 4 of W per thread)
-  const int g_row = tid >> 3, g_q = tid & 7;      // rows g_row + 32i, group g_q
-  const int w_n = tid >> 5, w_q = tid & 31;       // n rows w_n + 8i, float4 column w_q
-
-  v16f acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int x = 0; x < 16; ++x) acc[i][j][x] = 0.f;
-
-  const int nchunks = (N + BC - 1) / BC;
-
   for (int e = e_first; e <= e_last; ++e) {
     const int lo = max(clampi(off[e], 0, M), r0);
     const int hi = min(clampi(off[e + 1], 0, M), r0 + BM);
     if (hi <= lo) continue;
     const float *We = W + static_cast<size_t>(e) * N * K;
-
-    v4f greg[4], wreg[4];
-    auto load_chunk = [&](int c) {
-      const int n0 = c * BC;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = r0 + g_row + 32 * i;
-        const int n = n0 + 4 * g_q;
-        if (r >= lo && r < hi && n < N)
-          greg[i] = *reinterpret_cast<const v4f *>(G + static_cast<size_t>(r) * N + n);
-        else
-          greg[i] = (v4f){0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int n = n0 + w_n + 8 * i;
-        const int k = k0 + 4 * w_q;
-        if (n < N && k < K)
-          wreg[i] = *reinterpret_cast<const v4f *>(We + static_cast<size_t>(n) * K + k);
-        else
-          wreg[i] = (v4f){0.f, 0.f, 0.f, 0.f};
-      }
-    };
-    auto store_chunk = [&](int buf) {
-      uint8_t *st = smem + buf * STAGE;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<v4f *>(st + g_lds_off(g_row + 32 * i, g_q)) = greg[i];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<v4f *>(st + w_lds_off(w_n + 8 * i, 4 * w_q)) = wreg[i];
-    };
-
-    load_chunk(0);
-    store_chunk(0);
-    barrier();
-    for (int c = 0; c < nchunks; ++c) {
-      const int buf = c & 1;
-      if (c + 1 < nchunks) load_chunk(c + 1);
-      const uint8_t *st = smem + buf * STAGE;
-      // this lane's 16 g values per row block: n = 16h .. 16h+15
-      v4f ga[2][4];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int row = wr * 64 + i * 32 + l32;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          ga[i][q] = *reinterpret_cast<const v4f *>(st + g_lds_off(row, 4 * h + q));
-      }
-#pragma unroll
-      for (int s = 0; s < 16; ++s) {
-        float wb[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          wb[j] = *reinterpret_cast<const float *>(st + w_lds_off(16 * h + s, wc * 64 + j * 32 + l32));
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(ga[i][s >> 2][s & 3], wb[j], acc[i][j], 0, 0, 0);
-      }
-      if (c + 1 < nchunks) {
-        store_chunk(buf ^ 1);
-      }
-      barrier();
+    // the 32-row blocks [ib0, ib1) of the tile that hold this expert's rows
+    const int ib0 = __builtin_amdgcn_readfirstlane((lo - r0) >> 5);
+    const int ib1 = __builtin_amdgcn_readfirstlane((hi - r0 + 31) >> 5);
+    switch (ib1 - ib0) {
+      case 1: dgrad_pass<1>(G, We, DX, smem, M, N, K, r0, k0, lo, hi, ib0, tid, wave); break;
+      case 2: dgrad_pass<2>(G, We, DX, smem, M, N, K, r0, k0, lo, hi, ib0, tid, wave); break;
+      case 3: dgrad_pass<3>(G, We, DX, smem, M, N, K, r0, k0, lo, hi, ib0, tid, wave); break;
+      default: dgrad_pass<4>(G, We, DX, smem, M, N, K, r0, k0, lo, hi, ib0, tid, wave); break;
     }
   }
-
-  // store: register x of acc[i][j] is row wr*64 + i*32 + 8(x/4) + 4h + x%4, column wc*64 + j*32 + l32
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int col = k0 + wc * 64 + j * 32 + l32;
-      if (col >= K) continue;
-#pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        const int row = r0 + wr * 64 + i * 32 + 8 * (x >> 2) + 4 * h + (x & 3);
-        if (row < M) DX[static_cast<size_t>(row) * K + col] = acc[i][j][x];
+  // rows before off[0] or from off[E] on belong to no expert: +0.0
+  const int c0 = clampi(off[0], 0, M), c1 = max(c0, clampi(off[E], 0, M));
+  if (r0 < c0 || r_last >= c1) {
+    const int lane = tid & 63;
+    const int col = k0 + wave * 32 + (lane & 31);
+    if (col < K)
+      for (int rr = lane >> 5; rr < BM; rr += 2) {
+        const int row = r0 + rr;
+        if (row < M && (row < c0 || row >= c1)) DX[static_cast<size_t>(row) * K + col] = 0.f;
       }
-    }
+  }
 }
 
 __global__ void row_experts_kernel(const int32_t *__restrict__ off, int E, int M, int32_t *__restrict__ out) {

@@ -28,6 +28,8 @@ CASES = {
     "many_in_tile": (32, 128, [3, 1, 0, 5, 40, 2, 77, 0, 1]),
     "one_expert_odd": (36, 260, [300]),
     "long_n": (1000, 128, [129, 127]),
+    # passes over 32-row blocks (0,3), (2,4), (0,2), (1,3), (2,3) of their tiles; a partial column tile
+    "row_blocks": (160, 192, [70, 58, 40, 50, 38, 70, 20, 38]),
 }
 
 
