@@ -132,8 +132,6 @@ def test_scaled_mfma_layouts(probe):
                     break
             found[(shape, layout)] = ok
     print("scaled MFMA layout matches:", found, flush=True)
-    os.makedirs("gpurun_out", exist_ok=True)
-    np.savez("gpurun_out/mfma_probe_raw.npz", a=a, b=b, sa=sa, sb=sb, o16=o16, o32=o32)
     assert found[(16, KERNEL_ASSUMES)] and found[(32, KERNEL_ASSUMES)], found
 
 
