@@ -153,53 +153,74 @@ __global__ __launch_bounds__(256) void mx4_quantize_kernel(const float *__restri
   }
 }
 
-constexpr int QT_TOK = 128;                // tokens per transposed tile
-constexpr int QT_FEAT = 64;                // features per transposed tile
-constexpr int QT_PITCH = QT_TOK + 4;       // floats per LDS feature row
+constexpr int QT_TOK = 128;                // tokens per transposed tile (4 blocks of 32, one per wave)
+constexpr int QT_FEAT = 256;               // features per transposed tile (4 per lane)
+constexpr int QT_ROW = QT_TOK + 16;        // LDS bytes per staged feature row of codes (padded)
 
+// Wave w of a 256-thread workgroup takes the 32 tokens tok0 + 32w .. +31 of
+// the tile and lane l the features f0 + 4l .. +3: 32 float4 loads, one per
+// token, each wave-wide load reading 1 KB of a token row.  The four block
+// maxima, scales and codes come out of registers (codes of four consecutive
+// tokens of one feature at a time); only the codes and scale bytes go through
+// LDS, so that each feature row of the output leaves as one 128-byte line.
 template <bool ROUNDUP>
 __global__ __launch_bounds__(256) void mx_quantize_t_kernel(const float *__restrict__ X, uint8_t *__restrict__ Q,
                                                             uint8_t *__restrict__ S, int R, int L, int tiles_f) {
-  __shared__ __attribute__((aligned(16))) float tile[QT_FEAT * QT_PITCH];
+  __shared__ __attribute__((aligned(16))) uint8_t codes[QT_FEAT * QT_ROW];
+  __shared__ __attribute__((aligned(16))) uint8_t scales[QT_FEAT * 4];
   const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
   const int bt = blockIdx.x / tiles_f, bf = blockIdx.x - bt * tiles_f;
   const int tok0 = bt * QT_TOK, f0 = bf * QT_FEAT;
-  // 128 token rows of 64 features: 16 threads per row, 16 rows per pass
+  const int gt = tok0 + 32 * w;              // this wave's token block
+  const int gf = f0 + 4 * lane;              // this lane's first feature
+  if (gt < R && gf < L) {                    // R % 32 == 0 and L % 4 == 0: whole blocks and quads
+    v4f v[32];
+    const float *src = X + static_cast<size_t>(gt) * L + gf;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int idx = tid + 256 * i;
-    const int tok = idx >> 4, fq = idx & 15;
-    const int gt = tok0 + tok, gf = f0 + 4 * fq;
-    v4f v = {0.f, 0.f, 0.f, 0.f};
-    if (gt < R && gf < L)
-      v = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(X + static_cast<size_t>(gt) * L + gf));
+    for (int t = 0; t < 32; ++t) v[t] = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(src + static_cast<size_t>(t) * L));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) tile[(4 * fq + j) * QT_PITCH + tok] = v[j];
+    for (int j = 0; j < 4; ++j) {
+      uint32_t m = 0;
+#pragma unroll
+      for (int t = 0; t < 32; ++t) m = max(m, __float_as_uint(v[t][j]) & 0x7FFFFFFFu);
+      const uint32_t sb = scale_byte<ROUNDUP>(m);
+      v4u lo, hi;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lo[i] = e4m3x4((v4f){v[4 * i][j], v[4 * i + 1][j], v[4 * i + 2][j], v[4 * i + 3][j]}, sb);
+        hi[i] = e4m3x4((v4f){v[16 + 4 * i][j], v[16 + 4 * i + 1][j], v[16 + 4 * i + 2][j], v[16 + 4 * i + 3][j]}, sb);
+      }
+      uint8_t *dst = codes + (4 * lane + j) * QT_ROW + 32 * w;
+      *reinterpret_cast<v4u *>(dst) = lo;
+      *reinterpret_cast<v4u *>(dst + 16) = hi;
+      scales[(4 * lane + j) * 4 + w] = static_cast<uint8_t>(sb);
+    }
   }
   __syncthreads();
-  const int feat = tid >> 2, blk = tid & 3;
-  const int gf = f0 + feat, gt = tok0 + 32 * blk;
-  if (gf >= L || gt >= R) return;
-  const v4f *src = reinterpret_cast<const v4f *>(tile + feat * QT_PITCH + 32 * blk);
-  v4f v[8];
-  uint32_t m = 0;
+  // codes: 256 feature rows x 128 bytes, eight 16-byte pieces per row, a
+  // thread per piece and pass (a wave-wide store writes eight whole rows)
+  const int ntok = min(QT_TOK, R - tok0);    // a multiple of 32
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    v[i] = src[i];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) m = max(m, __float_as_uint(v[i][j]) & 0x7FFFFFFFu);
+  for (int p = 0; p < 8; ++p) {
+    const int fr = p * 32 + (tid >> 3), piece = tid & 7;
+    if (f0 + fr < L && 16 * piece < ntok) {
+      const v4u c = *reinterpret_cast<const v4u *>(codes + fr * QT_ROW + 16 * piece);
+      __builtin_nontemporal_store(c, reinterpret_cast<v4u *>(Q + static_cast<size_t>(f0 + fr) * R + tok0 + 16 * piece));
+    }
   }
-  const uint32_t sb = scale_byte<ROUNDUP>(m);
-  v4u lo, hi;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    lo[i] = e4m3x4(v[i], sb);
-    hi[i] = e4m3x4(v[4 + i], sb);
+  // scales: the tile's 4 bytes of each feature row (fewer at the end of R)
+  {
+    const int fr = tid;
+    if (f0 + fr < L) {
+      uint8_t *srow = S + static_cast<size_t>(f0 + fr) * (R / 32) + tok0 / 32;
+      if (ntok == QT_TOK && ((reinterpret_cast<uintptr_t>(srow) & 3u) == 0u)) {
+        *reinterpret_cast<uint32_t *>(srow) = *reinterpret_cast<const uint32_t *>(scales + fr * 4);
+      } else {
+        for (int b = 0; b < ntok / 32; ++b) srow[b] = scales[fr * 4 + b];
+      }
+    }
   }
-  uint8_t *dst = Q + static_cast<size_t>(gf) * R + gt;
-  __builtin_nontemporal_store(lo, reinterpret_cast<v4u *>(dst));
-  __builtin_nontemporal_store(hi, reinterpret_cast<v4u *>(dst + 16));
-  S[static_cast<size_t>(gf) * (R / 32) + gt / 32] = static_cast<uint8_t>(sb);
 }
 
 int launch_quantize_t(bool roundup, const float *X, uint8_t *Q, uint8_t *S, int R, int L, hipStream_t stream) {
