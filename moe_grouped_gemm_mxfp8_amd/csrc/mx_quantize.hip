@@ -23,8 +23,9 @@
 // a signed zero either way.
 //
 // mx_quantize: HBM-bound streaming kernel; rows never split a block (L % 32
-// == 0), so the [R][L] input is a flat sequence of blocks.  A wave handles 512
-// elements per step as two coalesced 1 KB float4 sweeps; the 8 lanes that
+// == 0), so the [R][L] input is a flat sequence of blocks.  A wave handles 1024
+// elements per step as four coalesced 1 KB float4 sweeps, all loads issued
+// before any block is converted; the 8 lanes that
 // share a block reduce its max with xor shuffles; each lane writes its 4 codes
 // as one dword and the first lane of each block the scale byte.
 //
@@ -80,18 +81,28 @@ __device__ __forceinline__ uint32_t e4m3x4(v4f v, uint32_t sb) {
   return static_cast<uint32_t>(w);
 }
 
+constexpr int Q_PARTS = 4;                     // 256-element parts per wave and step
+constexpr int Q_WAVE_STEP = 256 * Q_PARTS;
+
 template <bool ROUNDUP>
 __global__ __launch_bounds__(256) void mx_quantize_kernel(const float *__restrict__ X, uint8_t *__restrict__ Q,
                                                           uint8_t *__restrict__ S, int64_t total) {
   const int lane = threadIdx.x & 63;
   const int64_t wave_global = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
   const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 6;
-  for (int64_t base = wave_global * 512; base < total; base += nwaves * 512) {
+  for (int64_t base = wave_global * Q_WAVE_STEP; base < total; base += nwaves * Q_WAVE_STEP) {
+    // all of the step's loads first (4 KB per wave in flight), then the blocks
+    v4f vv[Q_PARTS];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int64_t i0 = base + half * 256 + 4 * lane;   // this lane's 4 elements
+    for (int part = 0; part < Q_PARTS; ++part) {
+      const int64_t i0 = base + part * 256 + 4 * lane;
+      vv[part] = i0 < total ? __builtin_nontemporal_load(reinterpret_cast<const v4f *>(X + i0)) : (v4f){0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int part = 0; part < Q_PARTS; ++part) {
+      const int64_t i0 = base + part * 256 + 4 * lane;   // this lane's 4 elements
       const bool live = i0 < total;                       // whole 32-blocks are live or not
-      v4f v = live ? __builtin_nontemporal_load(reinterpret_cast<const v4f *>(X + i0)) : (v4f){0.f, 0.f, 0.f, 0.f};
+      const v4f v = vv[part];
       uint32_t m = 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) m = max(m, __float_as_uint(v[i]) & 0x7FFFFFFFu);
@@ -123,12 +134,19 @@ __global__ __launch_bounds__(256) void mx4_quantize_kernel(const float *__restri
   const int lane = threadIdx.x & 63;
   const int64_t wave_global = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
   const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 6;
-  for (int64_t base = wave_global * 512; base < total; base += nwaves * 512) {
+  for (int64_t base = wave_global * Q_WAVE_STEP; base < total; base += nwaves * Q_WAVE_STEP) {
+    // all of the step's loads first (4 KB per wave in flight), then the blocks
+    v4f vv[Q_PARTS];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int64_t i0 = base + half * 256 + 4 * lane;   // this lane's 4 elements
+    for (int part = 0; part < Q_PARTS; ++part) {
+      const int64_t i0 = base + part * 256 + 4 * lane;
+      vv[part] = i0 < total ? __builtin_nontemporal_load(reinterpret_cast<const v4f *>(X + i0)) : (v4f){0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int part = 0; part < Q_PARTS; ++part) {
+      const int64_t i0 = base + part * 256 + 4 * lane;   // this lane's 4 elements
       const bool live = i0 < total;                       // whole 32-blocks are live or not
-      v4f v = live ? __builtin_nontemporal_load(reinterpret_cast<const v4f *>(X + i0)) : (v4f){0.f, 0.f, 0.f, 0.f};
+      const v4f v = vv[part];
       uint32_t m = 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) m = max(m, __float_as_uint(v[i]) & 0x7FFFFFFFu);
@@ -245,7 +263,7 @@ int launch_quantize(bool roundup, const float *X, uint8_t *Q, uint8_t *S, int R,
   if (hipGetDevice(&dev) != hipSuccess) return MOE_GG_ELAUNCH;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     return MOE_GG_ELAUNCH;
-  const int64_t waves_needed = (total + 511) / 512;
+  const int64_t waves_needed = (total + Q_WAVE_STEP - 1) / Q_WAVE_STEP;
   int64_t blocks = (waves_needed + 3) / 4;
   const int64_t cap = static_cast<int64_t>(cus) * 16;
   if (blocks > cap) blocks = cap;
@@ -265,7 +283,7 @@ int launch_quantize4(const float *X, uint8_t *Q, uint8_t *S, int R, int L, hipSt
   if (hipGetDevice(&dev) != hipSuccess) return MOE_GG_ELAUNCH;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     return MOE_GG_ELAUNCH;
-  const int64_t waves_needed = (total + 511) / 512;
+  const int64_t waves_needed = (total + Q_WAVE_STEP - 1) / Q_WAVE_STEP;
   int64_t blocks = (waves_needed + 3) / 4;
   const int64_t cap = static_cast<int64_t>(cus) * 16;
   if (blocks > cap) blocks = cap;
