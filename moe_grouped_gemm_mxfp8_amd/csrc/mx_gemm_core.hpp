@@ -36,7 +36,7 @@ constexpr int ST_G = ST_X + TILE_BYTES;       // g-role tile
 constexpr int ST_SX = ST_G + TILE_BYTES;      // x-role scale dwords [256]
 constexpr int ST_SG = ST_SX + TK * 4;         // g-role scale dwords [256]
 constexpr int STAGE_BYTES = ST_SG + TN * 4;   // 68608
-static_assert(128 * 512 <= STAGE_BYTES, "the epilogue stages 128 rows of 512 bytes in one buffer");
+static_assert(8 * 8192 <= STAGE_BYTES, "the epilogue stages eight 8 KB wave regions in one buffer");
 
 // LDS byte offset of row r (0..255) inside an operand tile.
 __device__ __forceinline__ uint32_t tile_row(int r) {
@@ -213,12 +213,15 @@ constexpr int STORES_PER_TILE = 16;           // 16-byte stores per lane per out
 // 2 (k) x 4 (n) patches of 128 x 64, MFMA output rows k, columns n): bf16
 // (round to nearest even) into C[n][k] through a buffer descriptor whose
 // byte offset 0 is the tile's element (0, 0) and whose row stride is ld
-// elements; stores past the descriptor's size are dropped.  The tile goes
-// through LDS stage stg (free: its last step has been read) so that every
-// store instruction writes whole 512-byte row segments -- partial-line
-// non-temporal stores measured several times slower.  Staging row r (of
-// 128) of half h is output row 128h + r, its 16-byte chunks XOR-swizzled by
-// (r mod 32).
+// elements; stores past the descriptor's size are dropped.  Each wave stages
+// its own patch in a private 8 KB region of stg (free: its last step has been
+// read), 64 columns at a time as 64 rows of 128 bytes with the 16-byte pieces
+// XOR-swizzled by (row mod 8), and reads it back as whole rows, so every
+// store instruction writes eight 128-byte row pieces (whole lines;
+// partial-line non-temporal stores measured several times slower).  One
+// workgroup barrier in all: a wave's LDS writes and reads of its own region
+// execute in order.  (Staging the tile in two halves shared by all waves,
+// with four barriers, measured 2-3% slower end to end.)
 __device__ __forceinline__ void store_tile(const v16f (&acc)[4][2], uint8_t *stg, __amdgpu_buffer_rsrc_t crsrc,
                                            uint32_t ld, int wk, int wn, int tid) {
   // recompute the lane coordinates here rather than keep them live across
@@ -226,39 +229,39 @@ __device__ __forceinline__ void store_tile(const v16f (&acc)[4][2], uint8_t *stg
   // that drains the next step's loads)
   int etid = tid;
   asm volatile("" : "+v"(etid));
-  const int el32 = etid & 31, eg = (etid >> 5) & 1;
+  const int lane = etid & 63, el32 = lane & 31, eg = lane >> 5;
+  uint8_t *reg = stg + (wk * 4 + wn) * 8192;
   barrier();                                   // all waves are done reading that buffer
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    if ((wn >> 1) == half) {
+  for (int c = 0; c < 2; ++c) {
+    // columns wk*128 + 64c .. +63: accumulators a = 2c, 2c + 1
+#pragma unroll
+    for (int a2 = 0; a2 < 2; ++a2)
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
-        const int r = (wn & 1) * 64 + b * 32 + el32;
+        const int rl = b * 32 + el32;
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int c = (wk * 128 + a * 32 + 8 * q) >> 3;       // 16-byte chunk of the row
-            const uint32_t lo = pack_bf16x2(acc[a][b][4 * q + 0], acc[a][b][4 * q + 1]);
-            const uint32_t hi = pack_bf16x2(acc[a][b][4 * q + 2], acc[a][b][4 * q + 3]);
-            typedef uint32_t u2 __attribute__((ext_vector_type(2)));
-            *reinterpret_cast<u2 *>(stg + r * 512 + ((c ^ (r & 31)) << 4) + 8 * eg) = (u2){lo, hi};
-          }
+        for (int j = 0; j < 4; ++j) {
+          const int a = 2 * c + a2, q = a2 * 4 + j;          // 16-byte piece of the 128-byte row
+          const uint32_t lo = pack_bf16x2(acc[a][b][4 * j + 0], acc[a][b][4 * j + 1]);
+          const uint32_t hi = pack_bf16x2(acc[a][b][4 * j + 2], acc[a][b][4 * j + 3]);
+          typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+          *reinterpret_cast<u2 *>(reg + rl * 128 + ((q ^ (rl & 7)) << 4) + 8 * eg) = (u2){lo, hi};
+        }
       }
-    }
-    barrier();
+    asm volatile("" ::: "memory");
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
-      const int r = p * 16 + (etid >> 5);
-      const int c = etid & 31;
-      const v4u v = *reinterpret_cast<const v4u *>(stg + r * 512 + ((c ^ (r & 31)) << 4));
+      const int row = p * 8 + (lane >> 3), q = lane & 7;
+      const v4u v = *reinterpret_cast<const v4u *>(reg + row * 128 + ((q ^ (row & 7)) << 4));
       __builtin_amdgcn_raw_buffer_store_b128(
-          v, crsrc, static_cast<int>((static_cast<uint32_t>(half * 128 + r) * ld + c * 8) * 2u), 0, 2);
+          v, crsrc,
+          static_cast<int>((static_cast<uint32_t>(wn * 64 + row) * ld + wk * 128 + c * 64 + q * 8) * 2u), 0, 2);
     }
-    // the second half overwrites the staging; after it, the next step's
-    // barrier precedes any load into this buffer
-    if (half == 0) barrier();
+    // the next chunk overwrites the region only after these reads (in order)
+    asm volatile("" ::: "memory");
   }
+  // the next step's barrier (which waits for LDS) precedes any load into stg
 }
 
 // +0.0 into the same 256 x 256 bf16 tile, whole 512-byte row segments.
