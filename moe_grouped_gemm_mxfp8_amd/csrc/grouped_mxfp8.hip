@@ -28,10 +28,10 @@
 //  * Each 128-element contraction step stages both tiles (32 KB each) and
 //    their scale dwords in LDS with buffer loads that write LDS directly,
 //    double-buffered; the workgroup walks the steps of all its tiles as one
-//    stream, and waves 4-7 issue all stage loads.  In a tile with fewer than
-//    256 token rows the waves whose 64 rows are all past the end skip their
-//    MFMAs; the wave layout puts token-row groups g and g + 2 on one SIMD so
-//    that the remaining work stays spread over the SIMDs.
+//    stream, and waves 4-7 issue all stage loads.  A partial row tile still
+//    runs all its MFMAs (on zeros past its last row): letting those waves skip
+//    them desynchronised the workgroups that share a weight tile and raised
+//    the L2 misses by a third for a 1.5% gain.
 //  * Rows past M read as zero (buffer-descriptor range) and their stores are
 //    dropped the same way, so M needs no padding.
 //  * a8w4 (the decode page's mfma_f4f8: fp4 weights times MXFP8 activations):
@@ -197,12 +197,7 @@ __global__ __launch_bounds__(NTHREAD, 1) void grouped_mxfp8_kernel(
     voff_x4[i] = static_cast<uint32_t>(64 * w4 + 4 * (lane >> 2) + i) * Kx + static_cast<uint32_t>(lane & 3) * 16u;
 
   // MFMA operand addressing
-  // Wave w takes x-role half wk = w % 2 and token-row group wn = w / 2, so the
-  // two waves on a SIMD (w and w + 4) hold token rows 64 wn and 64 (wn + 2):
-  // in a tile with at most 128 (64) token rows every SIMD keeps one (or half
-  // of them one) wave with work, and the waves past the last row skip their
-  // MFMAs.
-  const int wk = wave & 1, wn = wave >> 1;
+  const int wk = wave >> 2, wn = wave & 3;
   const int g = lane >> 5, l32 = lane & 31;
   uint32_t xrow[4], grow[2];
 #pragma unroll
@@ -248,27 +243,19 @@ __global__ __launch_bounds__(NTHREAD, 1) void grouped_mxfp8_kernel(
       for (int i = 0; i < 8; ++i)
         dma_b128(srd_x, voff_t[i], cpos, __builtin_amdgcn_readfirstlane(base + ST_X + (w4 * 8 + i) * BLK));
     }
-    const v4i srd_sx = make_srd(SB + wrow * scale_row, 256u * scale_row);
-    dma_b32(srd_sx, voff_s, cpos / 32, __builtin_amdgcn_readfirstlane(base + ST_SX + w4 * 256));
-    // token rows 64 w4 .. 64 w4 + 63 and their scales, unless all are past
-    // the tile's end (then no wave reads them: the waves of that row group
-    // skip their MFMAs); each wave counts the loads it issued
-    if (64u * static_cast<uint32_t>(w4) < rows) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        dma_b128(srd_g, voff_t[i], cpos, __builtin_amdgcn_readfirstlane(base + ST_G + (w4 * 8 + i) * BLK));
-      const v4i srd_sg = make_srd(SA + static_cast<size_t>(ld_t.m0) * scale_row, rows * scale_row);
-      dma_b32(srd_sg, voff_s, cpos / 32, __builtin_amdgcn_readfirstlane(base + ST_SG + w4 * 256));
-      ops += LOADS_PER_STEP;
-    } else {
-      ops += LOADS_PER_STEP - 9;
-    }
+    for (int i = 0; i < 8; ++i)
+      dma_b128(srd_g, voff_t[i], cpos, __builtin_amdgcn_readfirstlane(base + ST_G + (w4 * 8 + i) * BLK));
+    const v4i srd_sx = make_srd(SB + wrow * scale_row, 256u * scale_row);
+    const v4i srd_sg = make_srd(SA + static_cast<size_t>(ld_t.m0) * scale_row, rows * scale_row);
+    dma_b32(srd_sx, voff_s, cpos / 32, __builtin_amdgcn_readfirstlane(base + ST_SX + w4 * 256));
+    dma_b32(srd_sg, voff_s, cpos / 32, __builtin_amdgcn_readfirstlane(base + ST_SG + w4 * 256));
+    ops += LOADS_PER_STEP;
   };
   // wait until the loads of the step in buffer b have landed: every vector
   // memory instruction issued after them may still be in flight
   // (the counts that occur: a step's loads, a tile's stores, both, and a
-  // zero tile's stores on top; a step without token loads issues fewer, and
-  // any smaller count than the instructions issued since is also correct)
+  // zero tile's stores on top; any smaller count is also correct)
   auto wait_step = [&](int bf) __attribute__((always_inline)) {
     constexpr int L = LOADS_PER_STEP, S = STORES_PER_TILE;
     const int younger = ops - mark[bf];
@@ -318,8 +305,7 @@ __global__ __launch_bounds__(NTHREAD, 1) void grouped_mxfp8_kernel(
         advance();
       }
       const uint8_t *st = smem + buf * STAGE_BYTES;
-      if (wn * 64 < cur.rows)            // token rows past the tile's last are zero: nothing to add
-        compute_step<SPLIT, XFP4>(st, acc, xrow, grow, chunk_off, wk, wn, l32, g, 0, TT, 0, TN);
+      compute_step<SPLIT, XFP4>(st, acc, xrow, grow, chunk_off, wk, wn, l32, g, 0, TT, 0, TN);
       buf ^= 1;
     }
     // ---- epilogue: C[m0 + m][j0 + j] for the tile's rows; the descriptor
