@@ -42,12 +42,14 @@ KERNEL_SOURCES = {
     "dgrad": ["dgrad_f32.hip", "common.hpp"],
     "quantize": ["mx_quantize.hip", "common.hpp"],
     "quantize_t": ["mx_quantize.hip", "common.hpp"],
+    "quantize4": ["mx_quantize.hip", "common.hpp"],
     "grouped": ["grouped_mxfp8.hip", "mx_gemm_core.hpp", "common.hpp"],
     "forward": ["grouped_mxfp8.hip", "mx_gemm_core.hpp", "common.hpp"],
     "a8w4": ["grouped_mxfp8.hip", "mx_gemm_core.hpp", "common.hpp"],
 }
 KERNEL_NAMES = {"wgrad": "wgrad_mxfp8_kernel", "dgrad": "dgrad_f32_kernel", "quantize": "mx_quantize_kernel",
-                "quantize_t": "mx_quantize_t_kernel", "grouped": "grouped_mxfp8_kernel",
+                "quantize_t": "mx_quantize_t_kernel", "quantize4": "mx4_quantize_kernel",
+                "grouped": "grouped_mxfp8_kernel",
                 "forward": "grouped_mxfp8_kernel", "a8w4": "grouped_mxfp8_kernel"}
 
 
@@ -311,34 +313,46 @@ def bench_forward(torch, mg, idx, steps, warmup, cpu_baseline, fast=False, fp4=F
     return line
 
 
-def bench_quantize(torch, mg, idx, steps, warmup, cpu_baseline):
+def bench_quantize(torch, mg, idx, steps, warmup, cpu_baseline, rule="floor", fp4=False):
+    """The MX quantiser on x^T (MXFP8 with the floor or round-up scale rule, or MXFP4)."""
     inp = wl.make_wgrad_inputs(idx)
     d = torch.device("cuda:0")
     x = torch.from_numpy(inp["xT"]).to(d)
     R, L = x.shape
-    q = torch.empty((R, L), dtype=torch.uint8, device=d)
+    q = torch.empty((R, L // 2 if fp4 else L), dtype=torch.uint8, device=d)
     s = torch.empty((R, L // 32), dtype=torch.uint8, device=d)
-    ms = time_steps(torch, lambda: mg.mx_quantize(x, q, s), steps, warmup)
-    nbytes = 4 * R * L + R * L + R * L // 32
+    if fp4:
+        ms = time_steps(torch, lambda: mg.mx4_quantize(x, q, s), steps, warmup)
+        nbytes = 4 * R * L + R * L // 2 + R * L // 32
+    else:
+        ms = time_steps(torch, lambda: mg.mx_quantize(x, q, s, rule=rule), steps, warmup)
+        nbytes = 4 * R * L + R * L + R * L // 32
     gbs = nbytes / (ms * 1e-3) / 1e9
-    line = {"metric": f"GB/s, MX quantise of x^T, workload {idx}", "value": round(gbs, 1), "unit": "GB/s",
-            "ms_per_step": round(ms, 4), "dtype": "f32->e4m3+e8m0",
+    what = "MXFP4 quantise" if fp4 else ("MX quantise (round-up scale rule)" if rule == "roundup" else "MX quantise")
+    line = {"metric": f"GB/s, {what} of x^T, workload {idx}", "value": round(gbs, 1), "unit": "GB/s",
+            "ms_per_step": round(ms, 4), "dtype": "f32->e2m1+e8m0" if fp4 else "f32->e4m3+e8m0",
             "config": {"workload": wl.WORKLOADS[idx].name, "R": R, "L": L},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": read_traffic("quantize", idx)}}
+                         "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": read_traffic("quantize", idx) if (rule == "floor" and not fp4) else None}}
     if cpu_baseline:
         import oracle
         sub = inp["xT"][: max(1, R // 8)]
         t0 = time.perf_counter()
-        oracle.mx_quantize(sub)
+        if fp4:
+            oracle.mx4_quantize(sub)
+        else:
+            oracle.mx_quantize(sub, rule=rule)
         dt = time.perf_counter() - t0
-        line["cpu_baseline"] = {"value": round(5.03125 * sub.size / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+        per_elem = nbytes / (R * L)
+        line["cpu_baseline"] = {"value": round(per_elem * sub.size / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
                                 "kind": "oracle", "seconds": round(dt, 2), "cpu": cpu_info(),
-                                "sample": f"rows 0..{sub.shape[0]} of x^T (oracle.mx_quantize)"}
+                                "sample": f"rows 0..{sub.shape[0]} of x^T "
+                                          f"({'oracle.mx4_quantize' if fp4 else 'oracle.mx_quantize'})"}
     return line
 
 
-def bench_quantize_t(torch, mg, idx, steps, warmup, cpu_baseline):
+def bench_quantize_t(torch, mg, idx, steps, warmup, cpu_baseline, rule="floor"):
     """The transposing quantiser on g [M, N] -> g^T codes [N, M] (the weight gradient's A operand)."""
     inp = wl.make_wgrad_inputs(idx)
     d = torch.device("cuda:0")
@@ -347,19 +361,21 @@ def bench_quantize_t(torch, mg, idx, steps, warmup, cpu_baseline):
     R, L = g.shape
     q = torch.empty((L, R), dtype=torch.uint8, device=d)
     s = torch.empty((L, R // 32), dtype=torch.uint8, device=d)
-    ms = time_steps(torch, lambda: mg.mx_quantize_t(g, q, s), steps, warmup)
+    ms = time_steps(torch, lambda: mg.mx_quantize_t(g, q, s, rule=rule), steps, warmup)
     nbytes = 4 * R * L + R * L + R * L // 32
     gbs = nbytes / (ms * 1e-3) / 1e9
-    line = {"metric": f"GB/s, transposing MX quantise of g, workload {idx}", "value": round(gbs, 1), "unit": "GB/s",
+    what = "transposing MX quantise (round-up scale rule)" if rule == "roundup" else "transposing MX quantise"
+    line = {"metric": f"GB/s, {what} of g, workload {idx}", "value": round(gbs, 1), "unit": "GB/s",
             "ms_per_step": round(ms, 4), "dtype": "f32->e4m3+e8m0",
             "config": {"workload": wl.WORKLOADS[idx].name, "R": R, "L": L},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": read_traffic("quantize_t", idx)}}
+                         "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": read_traffic("quantize_t", idx) if rule == "floor" else None}}
     if cpu_baseline:
         import oracle
         sub = g[:, : max(32, L // 8)].cpu().numpy()
         t0 = time.perf_counter()
-        oracle.mx_quantize(np.ascontiguousarray(sub.T))
+        oracle.mx_quantize(np.ascontiguousarray(sub.T), rule=rule)
         dt = time.perf_counter() - t0
         line["cpu_baseline"] = {"value": round(5.03125 * sub.size / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
                                 "kind": "oracle", "seconds": round(dt, 2), "cpu": cpu_info(),
@@ -387,10 +403,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--pass", dest="pass_name", choices=["wgrad", "grouped", "forward", "a8w4", "dgrad", "quantize", "quantize_t", "copy"], default="wgrad")
+    ap.add_argument("--pass", dest="pass_name", choices=["wgrad", "grouped", "forward", "a8w4", "dgrad", "quantize", "quantize_t", "quantize4", "copy"], default="wgrad")
     ap.add_argument("--workload", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--fast", action="store_true", help="wgrad: the single-pass entry point")
+    ap.add_argument("--fast", action="store_true", help="GEMM passes: the single-pass entry point")
+    ap.add_argument("--rule", choices=["floor", "roundup"], default="floor", help="quantise passes: the scale rule")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -405,13 +422,15 @@ def main():
         sys.exit(1)
 
     idx = args.workload or {"wgrad": 4, "grouped": 5, "forward": 5, "a8w4": 5, "dgrad": 5, "quantize": 4,
-                            "quantize_t": 4, "copy": 0}[args.pass_name]
+                            "quantize_t": 4, "quantize4": 4, "copy": 0}[args.pass_name]
     fn = {"wgrad": bench_wgrad, "grouped": bench_grouped, "forward": bench_forward, "a8w4": bench_forward,
           "dgrad": bench_dgrad, "quantize": bench_quantize, "quantize_t": bench_quantize_t,
-          "copy": bench_copy}[args.pass_name]
+          "quantize4": bench_quantize, "copy": bench_copy}[args.pass_name]
     kw = {"fast": True} if (args.fast and args.pass_name in ("wgrad", "grouped", "forward", "a8w4")) else {}
-    if args.pass_name == "a8w4":
+    if args.pass_name in ("a8w4", "quantize4"):
         kw["fp4"] = True
+    if args.pass_name in ("quantize", "quantize_t") and args.rule != "floor":
+        kw["rule"] = args.rule
     line = fn(torch, mg, idx, args.steps, args.warmup, not args.no_cpu_baseline, **kw)
     line.update({"n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
                  "higher_is_better": True, "scaling": "weak", "vs_baseline": None,

@@ -41,10 +41,9 @@
 // nibble; the operand order of the gfx950 MFMA's format 4).  Scale
 // 2^(floor(log2(block max)) - 2), 2 being E2M1's largest exponent as 8 is
 // E4M3's, the byte clamped to [1, 254] (1 for a zero block).  Codes: nearest
-// E2M1 value, ties to the even code, saturating at +-6, sign kept; written
-// out as seven threshold comparisons on |y| (strict at the ties that round
-// down to an even code, inclusive at those that round up to one), which is
-// exact.  Same streaming layout as mx_quantize, 2 bytes of codes per lane.
+// E2M1 value, ties to the even code, saturating at +-6, sign kept (integer
+// rounding of the f32 bits, exact; see e2m1_code).  Same streaming layout as
+// mx_quantize, 2 bytes of codes per lane.
 #include "common.hpp"
 #include "../../include/moe_gg.h"
 
@@ -119,40 +118,51 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(const float *__restric
   }
 }
 
-// E2M1 code of y (4 bits): |y| against the midpoints 0.25, 0.75, 1.25, 1.75,
-// 2.5, 3.5 and 5 of the magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+// E2M1 code of y (4 bits), nearest with ties to the even code, +-6 beyond.
+// For |y| >= 1 the code is |y|'s f32 exponent and top mantissa bit after
+// rounding the mantissa to that one bit, ties to even (add 0x1FFFFF plus the
+// kept bit, shift by 22): codes 2..7 are exactly (biased exponent, bit) -
+// 252, and anything that rounds to 8 or more saturates to 7.  Below 1 the
+// codes 0, 1, 2 (0, 0.5, 1) are |y| against the midpoints 0.25 (to 0) and
+// 0.75 (to 1.0).  The sign bit is kept.
 __device__ __forceinline__ uint32_t e2m1_code(float y) {
-  const float a = __builtin_fabsf(y);
-  const uint32_t c = (a > 0.25f ? 1u : 0u) + (a >= 0.75f ? 1u : 0u) + (a > 1.25f ? 1u : 0u) +
-                     (a >= 1.75f ? 1u : 0u) + (a > 2.5f ? 1u : 0u) + (a >= 3.5f ? 1u : 0u) +
-                     (a > 5.0f ? 1u : 0u);
-  return c | ((__float_as_uint(y) >> 28) & 8u);
+  const uint32_t u = __float_as_uint(y) & 0x7FFFFFFFu;
+  const float a = __uint_as_float(u);
+  const uint32_t r = (u + 0x1FFFFFu + ((u >> 22) & 1u)) >> 22;
+  const uint32_t hi = min(r - 252u, 7u);
+  const uint32_t lo = (a > 0.25f ? 1u : 0u) + (a >= 0.75f ? 1u : 0u);
+  return (a >= 1.0f ? hi : lo) | ((__float_as_uint(y) >> 28) & 8u);
 }
 
 __global__ __launch_bounds__(256) void mx4_quantize_kernel(const float *__restrict__ X, uint8_t *__restrict__ Q,
                                                            uint8_t *__restrict__ S, int64_t total) {
+  // a lane takes 8 consecutive elements (two float4) and writes their codes
+  // as one dword; four lanes share a 32-element block
   const int lane = threadIdx.x & 63;
   const int64_t wave_global = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
   const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 6;
   for (int64_t base = wave_global * Q_WAVE_STEP; base < total; base += nwaves * Q_WAVE_STEP) {
-    // all of the step's loads first (4 KB per wave in flight), then the blocks
-    v4f vv[Q_PARTS];
+    v4f vv[Q_PARTS / 2][2];
 #pragma unroll
-    for (int part = 0; part < Q_PARTS; ++part) {
-      const int64_t i0 = base + part * 256 + 4 * lane;
-      vv[part] = i0 < total ? __builtin_nontemporal_load(reinterpret_cast<const v4f *>(X + i0)) : (v4f){0.f, 0.f, 0.f, 0.f};
+    for (int part = 0; part < Q_PARTS / 2; ++part) {
+      const int64_t i0 = base + part * 512 + 8 * lane;
+      const bool live = i0 < total;                       // whole 32-blocks are live or not
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        vv[part][h] = live ? __builtin_nontemporal_load(reinterpret_cast<const v4f *>(X + i0 + 4 * h))
+                           : (v4f){0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
-    for (int part = 0; part < Q_PARTS; ++part) {
-      const int64_t i0 = base + part * 256 + 4 * lane;   // this lane's 4 elements
-      const bool live = i0 < total;                       // whole 32-blocks are live or not
-      const v4f v = vv[part];
+    for (int part = 0; part < Q_PARTS / 2; ++part) {
+      const int64_t i0 = base + part * 512 + 8 * lane;
+      const bool live = i0 < total;
       uint32_t m = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) m = max(m, __float_as_uint(v[i]) & 0x7FFFFFFFu);
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m = max(m, __float_as_uint(vv[part][h][i]) & 0x7FFFFFFFu);
       m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 1)));
       m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 2)));
-      m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 4)));
       uint32_t sb = 1u;
       if (m != 0) {
         const int s = floor_log2_bits(m) - 2 + 127;
@@ -162,10 +172,12 @@ __global__ __launch_bounds__(256) void mx4_quantize_kernel(const float *__restri
       const float f = __uint_as_float((254u - sb) << 23);
       uint32_t codes = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) codes |= e2m1_code(v[i] * f) << (4 * i);
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) codes |= e2m1_code(vv[part][h][i] * f) << (4 * (4 * h + i));
       if (live) {
-        __builtin_nontemporal_store(static_cast<uint16_t>(codes), reinterpret_cast<uint16_t *>(Q + (i0 >> 1)));
-        if ((lane & 7) == 0) S[i0 >> 5] = static_cast<uint8_t>(sb);
+        __builtin_nontemporal_store(codes, reinterpret_cast<uint32_t *>(Q + (i0 >> 1)));
+        if ((lane & 3) == 0) S[i0 >> 5] = static_cast<uint8_t>(sb);
       }
     }
   }
