@@ -180,6 +180,29 @@ def test_wgrad_full_size_unaligned_offsets():
 
 # ---- the single-pass entry point (moe_gg_wgrad_mxfp8_fast) -------------------
 
+def test_wgrad_most_experts():
+    """E = 1024 (the limit of the kernel's on-chip expert ranking), most experts empty, the others
+    with 1..300 tokens at unaligned bounds; every expert's block against the oracle, empty ones +0.0."""
+    torch, mg = require_gpu()
+    rng = np.random.default_rng(1024)
+    E, N, K = 1024, 256, 256
+    counts = np.zeros(E, np.int64)
+    live = rng.choice(E, 12, replace=False)
+    counts[live] = rng.integers(1, 300, size=12)
+    M = int(np.ceil(counts.sum() / 128) * 128)
+    counts[live[-1]] += M - counts.sum()                    # M a multiple of 128
+    off = wl.offsets_from_counts(counts)
+    gT = rng.standard_normal((N, M)).astype(np.float32)
+    xT = rng.standard_normal((K, M)).astype(np.float32)
+    ca, sa, cb, sb = _mx_inputs(gT, xT)
+    say("wgrad E=1024", M, sorted(int(c) for c in counts[live]))
+    got = _run(torch, mg, ca, sa, cb, sb, off)
+    ref = oracle.wgrad(ca, sa, cb, sb, off)
+    assert oracle.wgrad_excess(got, ref) <= 0
+    empty = np.repeat(counts == 0, N)
+    assert np.all(got[empty] == 0.0)
+
+
 def _run_fast(torch, mg, ca, sa, cb, sb, off):
     out = mg.wgrad_mxfp8(dev(torch, ca), dev(torch, cb), dev(torch, sa), dev(torch, sb),
                          dev(torch, np.asarray(off, np.int32)), fast=True)
