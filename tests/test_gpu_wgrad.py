@@ -182,7 +182,12 @@ def test_wgrad_full_size_unaligned_offsets():
 
 def test_wgrad_most_experts():
     """E = 1024 (the limit of the kernel's on-chip expert ranking), most experts empty, the others
-    with 1..300 tokens at unaligned bounds; every expert's block against the oracle, empty ones +0.0."""
+    with 1..300 tokens at unaligned bounds; every expert's block against the oracle, empty ones +0.0.
+
+    The empty experts' blocks (1012 of 1024) are checked to be exactly zero, and the tolerance's
+    rms is taken over the non-empty experts' blocks: over the whole, mostly-zero output it is 9x
+    smaller than the values' scale (the matrix core's rounding, which the two-pass hardware model
+    reproduces exactly here, then exceeds it by 1.0e-4)."""
     torch, mg = require_gpu()
     rng = np.random.default_rng(1024)
     E, N, K = 1024, 256, 256
@@ -198,9 +203,9 @@ def test_wgrad_most_experts():
     say("wgrad E=1024", M, sorted(int(c) for c in counts[live]))
     got = _run(torch, mg, ca, sa, cb, sb, off)
     ref = oracle.wgrad(ca, sa, cb, sb, off)
-    assert oracle.wgrad_excess(got, ref) <= 0
     empty = np.repeat(counts == 0, N)
     assert np.all(got[empty] == 0.0)
+    assert oracle.wgrad_excess(got[~empty], ref[~empty]) <= 0
 
 
 def _run_fast(torch, mg, ca, sa, cb, sb, off):
