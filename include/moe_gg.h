@@ -276,6 +276,19 @@ MOE_GG_API int moe_gg_mx4_quantize(const float *X, uint8_t *Q, uint8_t *S, int R
                                    hipStream_t stream);
 
 /*
+ * Transposing MXFP4 quantiser: f32 X [R][L] -> E2M1 codes Q [L][R/2] (two per
+ * byte along R, the earlier element in the low nibble) + E8M0 scales
+ * S [L][R/32]; the same codes and scales as moe_gg_mx4_quantize of X^T.  With
+ * X = W_e [N][K] this gives the MXFP4 B[e] = W_e^T [K][N] along N that makes
+ * moe_gg_grouped_a8w4 an MXFP4-weight data gradient dx = g W_e.
+ *
+ * Inputs must be finite.  Shapes: R >= 32, R % 32 == 0, L >= 1 (EINVAL
+ * otherwise); L % 4 == 0 (EUNSUPPORTED otherwise).
+ */
+MOE_GG_API int moe_gg_mx4_quantize_t(const float *X, uint8_t *Q, uint8_t *S, int R, int L,
+                                     hipStream_t stream);
+
+/*
  * Row -> expert map, the integer step of the data gradient, exposed so that
  * it can be checked exactly: out[r] = the e with off[e] <= r < off[e+1] for r
  * in [0, M), computed by the same device function the data-gradient kernel

@@ -30,6 +30,7 @@ SIGNATURES = {
     "moe_gg_mx_quantize_t": (_I, [_VP, _VP, _VP, _I, _I, _VP]),
     "moe_gg_mx_quantize_roundup": (_I, [_VP, _VP, _VP, _I, _I, _VP]),
     "moe_gg_mx4_quantize": (_I, [_VP, _VP, _VP, _I, _I, _VP]),
+    "moe_gg_mx4_quantize_t": (_I, [_VP, _VP, _VP, _I, _I, _VP]),
     "moe_gg_mx_quantize_t_roundup": (_I, [_VP, _VP, _VP, _I, _I, _VP]),
     "moe_gg_row_experts": (_I, [_VP, _I, _I, _VP, _VP]),
     "moe_gg_status_string": (ctypes.c_char_p, [_I]),

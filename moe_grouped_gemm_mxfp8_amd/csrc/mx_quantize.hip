@@ -185,7 +185,13 @@ __global__ __launch_bounds__(256) void mx4_quantize_kernel(const float *__restri
 
 constexpr int QT_TOK = 128;                // tokens per transposed tile (4 blocks of 32, one per wave)
 constexpr int QT_FEAT = 256;               // features per transposed tile (4 per lane)
-constexpr int QT_ROW = QT_TOK + 16;        // LDS bytes per staged feature row of codes (padded)
+
+// The MXFP4 scale byte: floor(log2 max) - 2 + 127 in [1, 254], 1 for a zero block.
+__device__ __forceinline__ uint32_t scale_byte4(uint32_t amax_bits) {
+  if (amax_bits == 0) return 1u;
+  const int s = floor_log2_bits(amax_bits) - 2 + 127;
+  return static_cast<uint32_t>(s < 1 ? 1 : (s > 254 ? 254 : s));
+}
 
 // Wave w of a 256-thread workgroup takes the 32 tokens tok0 + 32w .. +31 of
 // the tile and lane l the features f0 + 4l .. +3: 32 float4 loads, one per
@@ -193,9 +199,14 @@ constexpr int QT_ROW = QT_TOK + 16;        // LDS bytes per staged feature row o
 // maxima, scales and codes come out of registers (codes of four consecutive
 // tokens of one feature at a time); only the codes and scale bytes go through
 // LDS, so that each feature row of the output leaves as one 128-byte line.
-template <bool ROUNDUP>
+// FMT: 0 E4M3 (floor rule), 1 E4M3 (round-up rule), 2 E2M1 (MXFP4: 64 bytes
+// of codes per feature row and tile, two per byte, the earlier token low).
+template <int FMT>
 __global__ __launch_bounds__(256) void mx_quantize_t_kernel(const float *__restrict__ X, uint8_t *__restrict__ Q,
                                                             uint8_t *__restrict__ S, int R, int L, int tiles_f) {
+  constexpr bool FP4 = FMT == 2;
+  constexpr int ROWB = FP4 ? QT_TOK / 2 : QT_TOK;   // code bytes of a feature row in the tile
+  constexpr int QT_ROW = ROWB + 16;                 // LDS bytes per staged feature row (padded)
   __shared__ __attribute__((aligned(16))) uint8_t codes[QT_FEAT * QT_ROW];
   __shared__ __attribute__((aligned(16))) uint8_t scales[QT_FEAT * 4];
   const int tid = threadIdx.x;
@@ -214,29 +225,48 @@ __global__ __launch_bounds__(256) void mx_quantize_t_kernel(const float *__restr
       uint32_t m = 0;
 #pragma unroll
       for (int t = 0; t < 32; ++t) m = max(m, __float_as_uint(v[t][j]) & 0x7FFFFFFFu);
-      const uint32_t sb = scale_byte<ROUNDUP>(m);
-      v4u lo, hi;
+      if constexpr (FP4) {
+        const uint32_t sb = scale_byte4(m);
+        const float f = __uint_as_float((254u - sb) << 23);   // 2^(127 - sb), sb <= 252
+        v4u c;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        lo[i] = e4m3x4((v4f){v[4 * i][j], v[4 * i + 1][j], v[4 * i + 2][j], v[4 * i + 3][j]}, sb);
-        hi[i] = e4m3x4((v4f){v[16 + 4 * i][j], v[16 + 4 * i + 1][j], v[16 + 4 * i + 2][j], v[16 + 4 * i + 3][j]}, sb);
+        for (int i = 0; i < 4; ++i) {
+          uint32_t word = 0;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) word |= e2m1_code(v[8 * i + k][j] * f) << (4 * k);
+          c[i] = word;
+        }
+        *reinterpret_cast<v4u *>(codes + (4 * lane + j) * QT_ROW + 16 * w) = c;
+        scales[(4 * lane + j) * 4 + w] = static_cast<uint8_t>(sb);
+      } else {
+        const uint32_t sb = scale_byte<FMT == 1>(m);
+        v4u lo, hi;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          lo[i] = e4m3x4((v4f){v[4 * i][j], v[4 * i + 1][j], v[4 * i + 2][j], v[4 * i + 3][j]}, sb);
+          hi[i] = e4m3x4((v4f){v[16 + 4 * i][j], v[16 + 4 * i + 1][j], v[16 + 4 * i + 2][j], v[16 + 4 * i + 3][j]}, sb);
+        }
+        uint8_t *dst = codes + (4 * lane + j) * QT_ROW + 32 * w;
+        *reinterpret_cast<v4u *>(dst) = lo;
+        *reinterpret_cast<v4u *>(dst + 16) = hi;
+        scales[(4 * lane + j) * 4 + w] = static_cast<uint8_t>(sb);
       }
-      uint8_t *dst = codes + (4 * lane + j) * QT_ROW + 32 * w;
-      *reinterpret_cast<v4u *>(dst) = lo;
-      *reinterpret_cast<v4u *>(dst + 16) = hi;
-      scales[(4 * lane + j) * 4 + w] = static_cast<uint8_t>(sb);
     }
   }
   __syncthreads();
-  // codes: 256 feature rows x 128 bytes, eight 16-byte pieces per row, a
-  // thread per piece and pass (a wave-wide store writes eight whole rows)
+  // codes: 256 feature rows of ROWB bytes as 16-byte pieces, a thread per
+  // piece and pass (a wave-wide store writes whole rows)
   const int ntok = min(QT_TOK, R - tok0);    // a multiple of 32
+  constexpr int PIECES = ROWB / 16;          // per row: 8 (E4M3) or 4 (E2M1)
+  constexpr int TOK_PER_PIECE = FP4 ? 32 : 16;
+  const size_t qrow = FP4 ? static_cast<size_t>(R) / 2 : static_cast<size_t>(R);
+  const size_t qcol = FP4 ? static_cast<size_t>(tok0) / 2 : static_cast<size_t>(tok0);
 #pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    const int fr = p * 32 + (tid >> 3), piece = tid & 7;
-    if (f0 + fr < L && 16 * piece < ntok) {
+  for (int p = 0; p < PIECES; ++p) {
+    const int fr = p * (256 / PIECES) + tid / PIECES, piece = tid % PIECES;
+    if (f0 + fr < L && TOK_PER_PIECE * piece < ntok) {
       const v4u c = *reinterpret_cast<const v4u *>(codes + fr * QT_ROW + 16 * piece);
-      __builtin_nontemporal_store(c, reinterpret_cast<v4u *>(Q + static_cast<size_t>(f0 + fr) * R + tok0 + 16 * piece));
+      __builtin_nontemporal_store(c, reinterpret_cast<v4u *>(Q + static_cast<size_t>(f0 + fr) * qrow + qcol + 16 * piece));
     }
   }
   // scales: the tile's 4 bytes of each feature row (fewer at the end of R)
@@ -253,18 +283,21 @@ __global__ __launch_bounds__(256) void mx_quantize_t_kernel(const float *__restr
   }
 }
 
-int launch_quantize_t(bool roundup, const float *X, uint8_t *Q, uint8_t *S, int R, int L, hipStream_t stream) {
+int launch_quantize_t(int fmt, const float *X, uint8_t *Q, uint8_t *S, int R, int L, hipStream_t stream) {
   if (!X || !Q || !S || R <= 0 || L <= 0 || R % 32) return MOE_GG_EINVAL;
   if (L % 4) return MOE_GG_EUNSUPPORTED;
   const int tiles_t = (R + QT_TOK - 1) / QT_TOK, tiles_f = (L + QT_FEAT - 1) / QT_FEAT;
   const int64_t blocks = static_cast<int64_t>(tiles_t) * tiles_f;
   if (blocks > 0x7FFFFFFF) return MOE_GG_EUNSUPPORTED;
-  if (roundup)
-    hipLaunchKernelGGL(mx_quantize_t_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, X, Q,
-                       S, R, L, tiles_f);
+  if (fmt == 2)
+    hipLaunchKernelGGL(mx_quantize_t_kernel<2>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, X, Q, S, R,
+                       L, tiles_f);
+  else if (fmt == 1)
+    hipLaunchKernelGGL(mx_quantize_t_kernel<1>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, X, Q, S, R,
+                       L, tiles_f);
   else
-    hipLaunchKernelGGL(mx_quantize_t_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, X, Q,
-                       S, R, L, tiles_f);
+    hipLaunchKernelGGL(mx_quantize_t_kernel<0>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, X, Q, S, R,
+                       L, tiles_f);
   return hipGetLastError() == hipSuccess ? MOE_GG_OK : MOE_GG_ELAUNCH;
 }
 
@@ -308,12 +341,12 @@ int launch_quantize4(const float *X, uint8_t *Q, uint8_t *S, int R, int L, hipSt
 
 extern "C" MOE_GG_API int moe_gg_mx_quantize_t(const float *X, uint8_t *Q, uint8_t *S, int R, int L,
                                                hipStream_t stream) {
-  return moe_gg::launch_quantize_t(false, X, Q, S, R, L, stream);
+  return moe_gg::launch_quantize_t(0, X, Q, S, R, L, stream);
 }
 
 extern "C" MOE_GG_API int moe_gg_mx_quantize_t_roundup(const float *X, uint8_t *Q, uint8_t *S, int R, int L,
                                                        hipStream_t stream) {
-  return moe_gg::launch_quantize_t(true, X, Q, S, R, L, stream);
+  return moe_gg::launch_quantize_t(1, X, Q, S, R, L, stream);
 }
 
 extern "C" MOE_GG_API int moe_gg_mx_quantize(const float *X, uint8_t *Q, uint8_t *S, int R, int L,
@@ -329,4 +362,9 @@ extern "C" MOE_GG_API int moe_gg_mx_quantize_roundup(const float *X, uint8_t *Q,
 extern "C" MOE_GG_API int moe_gg_mx4_quantize(const float *X, uint8_t *Q, uint8_t *S, int R, int L,
                                               hipStream_t stream) {
   return moe_gg::launch_quantize4(X, Q, S, R, L, stream);
+}
+
+extern "C" MOE_GG_API int moe_gg_mx4_quantize_t(const float *X, uint8_t *Q, uint8_t *S, int R, int L,
+                                                hipStream_t stream) {
+  return moe_gg::launch_quantize_t(2, X, Q, S, R, L, stream);
 }

@@ -6,7 +6,7 @@ import torch
 from ._lib import call
 
 __all__ = ["wgrad_mxfp8", "grouped_mxfp8", "dgrad_f32", "mx_quantize", "mx_quantize_t", "mx4_quantize",
-           "row_experts"]
+           "mx4_quantize_t", "row_experts"]
 
 
 def _stream() -> int:
@@ -145,6 +145,23 @@ def mx4_quantize(x, q=None, s=None):
     if q.numel() != R * (L // 2) or s.numel() != R * (L // 32):
         raise ValueError("q must hold R*L/2 bytes and s R*L/32")
     call("moe_gg_mx4_quantize", x.data_ptr(), q.data_ptr(), s.data_ptr(), R, L, _stream())
+    return q, s
+
+
+def mx4_quantize_t(x, q=None, s=None):
+    """MXFP4-quantise the transpose of f32 x[R, L] along R: (E2M1 codes uint8 [L, R/2], scales uint8 [L, R/32])."""
+    _dev(x, "x", (torch.float32,))
+    if x.dim() != 2:
+        raise ValueError("x must be [R, L]")
+    R, L = x.shape
+    if q is None:
+        q = torch.empty((L, max(R // 2, 1)), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty((L, max(R // 32, 1)), dtype=torch.uint8, device=x.device)
+    _dev(q, "q", _U8); _dev(s, "s", _U8)
+    if q.numel() != L * (R // 2) or s.numel() != L * (R // 32):
+        raise ValueError("q must hold L*R/2 bytes and s L*R/32")
+    call("moe_gg_mx4_quantize_t", x.data_ptr(), q.data_ptr(), s.data_ptr(), R, L, _stream())
     return q, s
 
 

@@ -30,7 +30,7 @@ def test_header_declares_the_entry_points():
     for want in ("moe_gg_wgrad_mxfp8", "moe_gg_wgrad_mxfp8_fast", "moe_gg_grouped_mxfp8",
                  "moe_gg_grouped_mxfp8_fast", "moe_gg_dgrad_f32", "moe_gg_mx_quantize",
                  "moe_gg_mx_quantize_t", "moe_gg_mx_quantize_roundup", "moe_gg_mx_quantize_t_roundup",
-                 "moe_gg_grouped_a8w4", "moe_gg_grouped_a8w4_fast", "moe_gg_mx4_quantize",
+                 "moe_gg_grouped_a8w4", "moe_gg_grouped_a8w4_fast", "moe_gg_mx4_quantize", "moe_gg_mx4_quantize_t",
                  "moe_gg_row_experts", "moe_gg_status_string"):
         assert want in names
 
@@ -108,6 +108,9 @@ def test_host_validation_dgrad_quantize_rows(lib):
     assert lib.moe_gg_mx4_quantize(p, p, None, 4, 64, None) == -1
     assert lib.moe_gg_mx4_quantize(p, p, p, 4, 48, None) == -1
     assert lib.moe_gg_mx4_quantize(p, p, p, 0, 64, None) == -1
+    assert lib.moe_gg_mx4_quantize_t(p, p, None, 64, 8, None) == -1
+    assert lib.moe_gg_mx4_quantize_t(p, p, p, 48, 8, None) == -1     # R % 32
+    assert lib.moe_gg_mx4_quantize_t(p, p, p, 64, 6, None) == -2     # L % 4
     assert lib.moe_gg_row_experts(p, 0, 10, p, None) == -1
     assert lib.moe_gg_row_experts(None, 2, 10, p, None) == -1
 

@@ -164,3 +164,44 @@ def test_a8w4_forward_full_size_sampled():
     ref = oracle.grouped_gemm_rows(ca, sa, cb, sb, off, rows, b_format="e2m1")
     out = host(got[rows]).astype(np.float64)
     assert oracle.wgrad_excess(out, ref, ref_rms=np.sqrt(np.mean(ref * ref))) <= 0
+
+
+@pytest.mark.parametrize("case", ["edges", "tile", "ragged"])
+def test_mx4_quantize_transposed_bit_exact(case):
+    """moe_gg_mx4_quantize_t(x) equals the oracle's MXFP4 quantisation of x^T, code for code."""
+    torch, mg = require_gpu()
+    rng = np.random.default_rng({"edges": 21, "tile": 22, "ragged": 23}[case])
+    if case == "edges":
+        x = np.ascontiguousarray(np.concatenate([_mx4_edges(), np.zeros((2, 128), np.float32)]).T)   # [128, 12]
+    elif case == "tile":
+        x = rng.standard_normal((256, 512)).astype(np.float32)
+    else:                                                     # partial tiles in both directions
+        x = (rng.standard_normal((160, 300)) * np.exp2(rng.integers(-40, 40, (1, 300)))).astype(np.float32)
+    say("mx4_quantize_t", case, x.shape)
+    q, s = mg.mx4_quantize_t(dev(torch, x))
+    torch.cuda.synchronize()
+    want_q, want_s = oracle.mx4_quantize(np.ascontiguousarray(x.T))
+    assert np.array_equal(host(s), want_s)
+    assert np.array_equal(host(q), want_q)
+
+
+def test_a8w4_as_data_gradient():
+    """dx = g W_e with MXFP4 weights: A = MX(g) along N, B[e] = MXFP4(W_e^T) along N from the transposing
+    MXFP4 quantiser (workload 2: E=8, M=4096, N=1024, K=2048, one empty expert)."""
+    torch, mg = require_gpu()
+    inp = wl.make_dgrad_inputs(2)
+    g, W, off = inp["g"], inp["W"], inp["off"]
+    E, N, K = W.shape
+    ca, sa = oracle.mx_quantize(g)
+    Wt = np.ascontiguousarray(np.transpose(W, (0, 2, 1)))    # [E, K, N]
+    cb, sb = _quant_b4(Wt)                                     # the oracle's codes of W_e^T
+    tq = torch.empty((E, K, N // 2), dtype=torch.uint8, device="cuda")
+    ts = torch.empty((E, K, N // 32), dtype=torch.uint8, device="cuda")
+    for e in range(E):
+        mg.mx4_quantize_t(dev(torch, W[e]), tq[e], ts[e])     # the GPU's, from W_e [N, K]
+    torch.cuda.synchronize()
+    assert np.array_equal(host(tq), cb) and np.array_equal(host(ts), sb)
+    say("a8w4 data gradient, workload 2")
+    got = _run(torch, mg, ca, sa, cb, sb, off)
+    ref = oracle.grouped_gemm(ca, sa, cb, sb, off, b_format="e2m1")
+    assert oracle.wgrad_excess(got, ref) <= 0
