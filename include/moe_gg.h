@@ -24,6 +24,10 @@
  *     off[0] = 0, off[e] <= off[e+1], off[E] = M; a malformed array yields
  *     unspecified values but no access outside the buffers (each bound is
  *     clamped to [0, M], a decreasing pair counts as empty).
+ *   - Debugging aid: with MOE_GG_VALIDATE=1 in the environment (read at each
+ *     call), the weight gradient, data gradient and grouped GEMM entry points
+ *     copy `expert_off` to the host, synchronising `stream`, and return
+ *     MOE_GG_EINVAL before launching if the offsets break those rules.
  */
 #ifndef MOE_GG_H
 #define MOE_GG_H

@@ -6,6 +6,11 @@
 
 namespace moe_gg {
 
+// Host: with MOE_GG_VALIDATE=1, copy the offsets to the host (synchronising
+// the stream) and return MOE_GG_EINVAL unless off[0] = 0, off[e] <= off[e+1]
+// and off[E] = M; otherwise MOE_GG_OK without touching them (status.cpp).
+int check_offsets_if_asked(const int32_t *off, int E, int M, hipStream_t stream);
+
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));

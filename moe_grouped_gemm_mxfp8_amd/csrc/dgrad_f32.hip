@@ -199,6 +199,7 @@ extern "C" MOE_GG_API int moe_gg_dgrad_f32(const float *A, const float *B, float
   if (!A || !B || !C || !expert_off) return MOE_GG_EINVAL;
   if (M <= 0 || N <= 0 || K <= 0 || E <= 0) return MOE_GG_EINVAL;
   if (K % 4 || N % 4) return MOE_GG_EUNSUPPORTED;
+  if (const int st = check_offsets_if_asked(expert_off, E, M, stream)) return st;
   const dim3 grid((K + BK - 1) / BK, (M + BM - 1) / BM);
   if (grid.y > 65535u) return MOE_GG_EUNSUPPORTED;
   hipLaunchKernelGGL(dgrad_f32_kernel, grid, dim3(NTHREAD), 0, stream, A, B, C, expert_off, M, N, K, E);

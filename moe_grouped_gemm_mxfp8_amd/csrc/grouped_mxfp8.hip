@@ -334,6 +334,7 @@ int launch_grouped(bool split, bool xfp4, const uint8_t *A, const uint8_t *B, ui
   // the rows of no expert before and after
   const int64_t total = (static_cast<int64_t>((M + TN - 1) / TN) + E + 2) * (N / TK);
   if (total > 0x7FFFFFFF) return MOE_GG_EUNSUPPORTED;
+  if (const int st = check_offsets_if_asked(expert_off, E, M, stream)) return st;
   const int grid = static_cast<int>(total < cus ? total : cus);
 #define MOE_GG_LAUNCH(S, X)                                                                              \
   hipLaunchKernelGGL((grouped_mxfp8_kernel<S, X>), dim3(grid), dim3(NTHREAD), 0, stream, A, B, C, scale_A, \

@@ -300,6 +300,7 @@ int launch_wgrad(bool split, const uint8_t *A, const uint8_t *B, uint16_t *C, co
     return MOE_GG_ELAUNCH;
   const int64_t total = static_cast<int64_t>(E) * (N / TN) * (K / TK);
   if (total > 0x7FFFFFFF) return MOE_GG_EUNSUPPORTED;
+  if (const int st = check_offsets_if_asked(expert_off, E, M, stream)) return st;
   const int grid = static_cast<int>(total < cus ? total : cus);
   if (split)
     hipLaunchKernelGGL(wgrad_mxfp8_kernel<true>, dim3(grid), dim3(NTHREAD), 0, stream, A, B, C, scale_A,

@@ -52,3 +52,14 @@ def test_small_inputs_shapes_and_determinism():
     assert abs(float(d2["W"].std()) - 1 / 32) < 1e-3
     w3 = wl.make_wgrad_inputs(3)
     assert w3["gT"].shape == (2048, 2048)
+
+
+def test_forward_inputs_shapes_offsets_and_determinism():
+    a = wl.make_forward_inputs(1)
+    b = wl.make_forward_inputs(1)
+    assert a["x"].shape == (256, 256) and a["W"].shape == (2, 256, 256)
+    assert a["x"].dtype == np.float32 and a["x"].flags.c_contiguous
+    assert np.array_equal(a["x"], b["x"]) and np.array_equal(a["W"], b["W"])
+    # the offsets are the workload's own draw, shared with its other passes
+    assert np.array_equal(wl.make_forward_inputs(2)["off"], wl.make_dgrad_inputs(2)["off"])
+    assert abs(float(a["W"].std()) - 0.02) < 2e-3
