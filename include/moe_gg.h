@@ -69,7 +69,9 @@ enum {
  *   accumulated in f32.
  *
  * Shapes: M, N, K, E >= 1; M % 128 == 0 (EINVAL otherwise);
- * N % 256 == 0 and K % 256 == 0 and E <= 1024 (EUNSUPPORTED otherwise).
+ * N % 256 == 0, K % 256 == 0, E <= 1024, 256 M < 2^32 and 512 K < 2^31
+ * (EUNSUPPORTED otherwise: 32-bit offsets inside an operand panel and an
+ * output tile).
  * Expert bounds need not be multiples of 128 (nor of 32): an expert's first
  * and last 128-token steps zero the g^T codes of the tokens outside it, so a
  * scale block shared by two experts contributes its own tokens to each.

@@ -294,6 +294,8 @@ int launch_wgrad(bool split, const uint8_t *A, const uint8_t *B, uint16_t *C, co
   if (N % TN || K % TK || E > MAX_EXPERTS) return MOE_GG_EUNSUPPORTED;
   // the buffer descriptors address one 256-row operand panel with 32-bit offsets
   if (static_cast<uint64_t>(TK) * static_cast<uint64_t>(M) > 0xFFFFFFFFull) return MOE_GG_EUNSUPPORTED;
+  // and one 256-row tile of the bf16 output (a signed 32-bit size)
+  if (static_cast<uint64_t>(TN) * static_cast<uint64_t>(K) * 2u > 0x7FFFFFFFull) return MOE_GG_EUNSUPPORTED;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return MOE_GG_ELAUNCH;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)

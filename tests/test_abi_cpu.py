@@ -70,6 +70,8 @@ def test_host_validation_wgrad(lib, name):
     assert f(p, p, p, p, p, p, 256, 200, 256, 2, None) == -2       # N % 256
     assert f(p, p, p, p, p, p, 256, 256, 384, 2, None) == -2       # K % 256
     assert f(p, p, p, p, p, p, 256, 256, 256, 2000, None) == -2    # E above the ranking table
+    assert f(p, p, p, p, p, p, 1 << 24, 256, 256, 2, None) == -2    # 256 rows x M beyond 32-bit offsets
+    assert f(p, p, p, p, p, p, 256, 256, 1 << 22, 2, None) == -2    # a 256-row bf16 output tile beyond 2^31 B
 
 
 @pytest.mark.parametrize("name", ["moe_gg_grouped_mxfp8", "moe_gg_grouped_mxfp8_fast", "moe_gg_grouped_a8w4",
