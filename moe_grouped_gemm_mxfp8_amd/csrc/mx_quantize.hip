@@ -41,9 +41,9 @@
 // nibble; the operand order of the gfx950 MFMA's format 4).  Scale
 // 2^(floor(log2(block max)) - 2), 2 being E2M1's largest exponent as 8 is
 // E4M3's, the byte clamped to [1, 254] (1 for a zero block).  Codes: nearest
-// E2M1 value, ties to the even code, saturating at +-6, sign kept (integer
-// rounding of the f32 bits, exact; see e2m1_code).  Same streaming layout as
-// mx_quantize, 2 bytes of codes per lane.
+// E2M1 value, ties to the even code, saturating at +-6, sign kept, by the
+// hardware's scaled conversion (see e2m1x8).  A lane takes 8 elements and
+// writes their codes as one dword.
 #include "common.hpp"
 #include "../../include/moe_gg.h"
 
@@ -118,20 +118,19 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(const float *__restric
   }
 }
 
-// E2M1 code of y (4 bits), nearest with ties to the even code, +-6 beyond.
-// For |y| >= 1 the code is |y|'s f32 exponent and top mantissa bit after
-// rounding the mantissa to that one bit, ties to even (add 0x1FFFFF plus the
-// kept bit, shift by 22): codes 2..7 are exactly (biased exponent, bit) -
-// 252, and anything that rounds to 8 or more saturates to 7.  Below 1 the
-// codes 0, 1, 2 (0, 0.5, 1) are |y| against the midpoints 0.25 (to 0) and
-// 0.75 (to 1.0).  The sign bit is kept.
-__device__ __forceinline__ uint32_t e2m1_code(float y) {
-  const uint32_t u = __float_as_uint(y) & 0x7FFFFFFFu;
-  const float a = __uint_as_float(u);
-  const uint32_t r = (u + 0x1FFFFFu + ((u >> 22) & 1u)) >> 22;
-  const uint32_t hi = min(r - 252u, 7u);
-  const uint32_t lo = (a > 0.25f ? 1u : 0u) + (a >= 0.75f ? 1u : 0u);
-  return (a >= 1.0f ? hi : lo) | ((__float_as_uint(y) >> 28) & 8u);
+// Eight E2M1 codes (a dword, element 2i in the low nibble of byte i) of
+// a[0..7] / scale: v_cvt_scalef32_pk_fp4_f32 divides by the scale and rounds
+// to nearest even with saturation at +-6, keeping the sign of zero; measured
+// on gfx950 to equal the oracle's rounding code for code on every tie, its
+// f32 neighbours, a dense sweep, signed zeros, subnormals and huge values at
+// scales 2^-10 .. 2^10.  With scale = 2^(sb - 127) (an exact power of two)
+// this is the MXFP4 quantiser's code step.
+__device__ __forceinline__ uint32_t e2m1x8(const float (&a)[8], float scale) {
+  uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a[0], a[1], scale, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a[2], a[3], scale, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a[4], a[5], scale, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a[6], a[7], scale, 3);
+  return w;
 }
 
 __global__ __launch_bounds__(256) void mx4_quantize_kernel(const float *__restrict__ X, uint8_t *__restrict__ Q,
@@ -168,13 +167,9 @@ __global__ __launch_bounds__(256) void mx4_quantize_kernel(const float *__restri
         const int s = floor_log2_bits(m) - 2 + 127;
         sb = static_cast<uint32_t>(s < 1 ? 1 : (s > 254 ? 254 : s));
       }
-      // 2^(127 - sb) with sb <= 252 for a finite max: a normal f32
-      const float f = __uint_as_float((254u - sb) << 23);
-      uint32_t codes = 0;
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) codes |= e2m1_code(vv[part][h][i] * f) << (4 * (4 * h + i));
+      const float a[8] = {vv[part][0][0], vv[part][0][1], vv[part][0][2], vv[part][0][3],
+                          vv[part][1][0], vv[part][1][1], vv[part][1][2], vv[part][1][3]};
+      const uint32_t codes = e2m1x8(a, __uint_as_float(sb << 23));   // divided by 2^(sb - 127)
       if (live) {
         __builtin_nontemporal_store(codes, reinterpret_cast<uint32_t *>(Q + (i0 >> 1)));
         if ((lane & 3) == 0) S[i0 >> 5] = static_cast<uint8_t>(sb);
@@ -227,14 +222,13 @@ __global__ __launch_bounds__(256) void mx_quantize_t_kernel(const float *__restr
       for (int t = 0; t < 32; ++t) m = max(m, __float_as_uint(v[t][j]) & 0x7FFFFFFFu);
       if constexpr (FP4) {
         const uint32_t sb = scale_byte4(m);
-        const float f = __uint_as_float((254u - sb) << 23);   // 2^(127 - sb), sb <= 252
+        const float scale = __uint_as_float(sb << 23);          // 2^(sb - 127)
         v4u c;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          uint32_t word = 0;
-#pragma unroll
-          for (int k = 0; k < 8; ++k) word |= e2m1_code(v[8 * i + k][j] * f) << (4 * k);
-          c[i] = word;
+          const float a[8] = {v[8 * i][j],     v[8 * i + 1][j], v[8 * i + 2][j], v[8 * i + 3][j],
+                              v[8 * i + 4][j], v[8 * i + 5][j], v[8 * i + 6][j], v[8 * i + 7][j]};
+          c[i] = e2m1x8(a, scale);
         }
         *reinterpret_cast<v4u *>(codes + (4 * lane + j) * QT_ROW + 16 * w) = c;
         scales[(4 * lane + j) * 4 + w] = static_cast<uint8_t>(sb);
