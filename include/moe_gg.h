@@ -24,6 +24,12 @@
  *     off[0] = 0, off[e] <= off[e+1], off[E] = M; a malformed array yields
  *     unspecified values but no access outside the buffers (each bound is
  *     clamped to [0, M], a decreasing pair counts as empty).
+ *   - Empty sizes: a size of 0 is valid (a negative size, or E < 1, is
+ *     MOE_GG_EINVAL).  A call whose output has no element returns MOE_GG_OK
+ *     and enqueues nothing.  A call whose contraction is empty (no tokens,
+ *     M = 0, for the weight gradient; N = 0 for the data gradient; K = 0 for
+ *     the grouped GEMM) writes zeros: the empty sum.  A pointer to a buffer of
+ *     zero size may be NULL; expert_off may not.
  *   - Debugging aid: with MOE_GG_VALIDATE=1 in the environment (read at each
  *     call), the weight gradient, data gradient and grouped GEMM entry points
  *     copy `expert_off` to the host, synchronising `stream`, and return
@@ -43,7 +49,7 @@ extern "C" {
 
 enum {
   MOE_GG_OK = 0,
-  MOE_GG_EINVAL = -1,       /* null pointer, non-positive size, misaligned size   */
+  MOE_GG_EINVAL = -1,       /* null pointer, negative size, misaligned size       */
   MOE_GG_EUNSUPPORTED = -2, /* valid request outside what the kernels tile        */
   MOE_GG_ELAUNCH = -3       /* the HIP runtime refused the launch                 */
 };
@@ -68,7 +74,8 @@ enum {
  *                        e4m3(A[n][m]) 2^(sA[n][m/32]-127) e4m3(B[k][m]) 2^(sB[k][m/32]-127) )
  *   accumulated in f32.
  *
- * Shapes: M, N, K, E >= 1; M % 128 == 0 (EINVAL otherwise);
+ * Shapes: M, N, K >= 0, E >= 1; M % 128 == 0 (EINVAL otherwise; M = 0
+ * writes +0.0 everywhere);
  * N % 256 == 0, K % 256 == 0, E <= 1024, 256 M < 2^32 and 512 K < 2^31
  * (EUNSUPPORTED otherwise: 32-bit offsets inside an operand panel and an
  * output tile).
@@ -124,8 +131,8 @@ MOE_GG_API int moe_gg_wgrad_mxfp8_fast(const uint8_t *A, const uint8_t *B, uint1
  *   dx[r][k] = sum_n g[r][n] W[e(r)][n][k],  e(r) the e with off[e] <= r < off[e+1],
  *   f32 products and f32 accumulation.
  *
- * Shapes: M, N, K, E >= 1 (EINVAL otherwise); K % 4 == 0 and N % 4 == 0
- * (EUNSUPPORTED otherwise).
+ * Shapes: M, N, K >= 0, E >= 1 (EINVAL otherwise; N = 0 writes zeros);
+ * K % 4 == 0 and N % 4 == 0 (EUNSUPPORTED otherwise).
  */
 MOE_GG_API int moe_gg_dgrad_f32(const float *A, const float *B, float *C,
                                 const int32_t *expert_off, int M, int N, int K, int E,
@@ -157,7 +164,8 @@ MOE_GG_API int moe_gg_dgrad_f32(const float *A, const float *B, float *C,
  * Data gradient dx = g W_e with W_e [N][K]: A = MX(g) along N (this call's K
  * is N), B[e] = moe_gg_mx_quantize_t(W_e) ([K][N] along N).
  *
- * Shapes: M, N, K, E >= 1 and K % 32 == 0 (EINVAL otherwise); N % 256 == 0,
+ * Shapes: M, N, K >= 0, E >= 1 and K % 32 == 0 (EINVAL otherwise; K = 0
+ * writes +0.0 everywhere); N % 256 == 0,
  * K % 128 == 0 and E <= 2048 (EUNSUPPORTED otherwise).  Accuracy as for the weight
  * gradient: this entry point splits A's codes into two MFMA passes (codes of
  * magnitude >= 128 and the rest), which keeps the result within
@@ -221,7 +229,7 @@ MOE_GG_API int moe_gg_grouped_a8w4_fast(const uint8_t *A, const uint8_t *B, uint
  *   Q[r][i] = e4m3_rne_saturate(X[r][i] * 2^(127 - s)); the sign of zero is kept
  *
  * Inputs must be finite (NaN/Inf give unspecified codes).
- * Shapes: R >= 1, L >= 32, L % 32 == 0 (EINVAL otherwise).
+ * Shapes: R, L >= 0, L % 32 == 0 (EINVAL otherwise).
  */
 MOE_GG_API int moe_gg_mx_quantize(const float *X, uint8_t *Q, uint8_t *S, int R, int L,
                                   hipStream_t stream);
@@ -237,7 +245,7 @@ MOE_GG_API int moe_gg_mx_quantize(const float *X, uint8_t *Q, uint8_t *S, int R,
  *   Q[l][r] and S[l][r/32] equal moe_gg_mx_quantize's output for the
  *   transpose X^T [L][R].
  *
- * Inputs must be finite.  Shapes: R >= 32, R % 32 == 0, L >= 1 (EINVAL
+ * Inputs must be finite.  Shapes: R, L >= 0, R % 32 == 0 (EINVAL
  * otherwise); L % 4 == 0 (EUNSUPPORTED otherwise: the loads are float4).
  */
 MOE_GG_API int moe_gg_mx_quantize_t(const float *X, uint8_t *Q, uint8_t *S, int R, int L,
@@ -275,7 +283,7 @@ MOE_GG_API int moe_gg_mx_quantize_t_roundup(const float *X, uint8_t *Q, uint8_t 
  *   code = e2m1_rne_saturate(X * 2^(127 - s)): nearest of 0, 0.5, 1, 1.5, 2,
  *          3, 4, 6, ties to the even code, +-6 beyond; sign bit kept
  *
- * Inputs must be finite.  Shapes: R >= 1, L >= 32, L % 32 == 0 (EINVAL
+ * Inputs must be finite.  Shapes: R, L >= 0, L % 32 == 0 (EINVAL
  * otherwise).
  */
 MOE_GG_API int moe_gg_mx4_quantize(const float *X, uint8_t *Q, uint8_t *S, int R, int L,
@@ -288,7 +296,7 @@ MOE_GG_API int moe_gg_mx4_quantize(const float *X, uint8_t *Q, uint8_t *S, int R
  * X = W_e [N][K] this gives the MXFP4 B[e] = W_e^T [K][N] along N that makes
  * moe_gg_grouped_a8w4 an MXFP4-weight data gradient dx = g W_e.
  *
- * Inputs must be finite.  Shapes: R >= 32, R % 32 == 0, L >= 1 (EINVAL
+ * Inputs must be finite.  Shapes: R, L >= 0, R % 32 == 0 (EINVAL
  * otherwise); L % 4 == 0 (EUNSUPPORTED otherwise).
  */
 MOE_GG_API int moe_gg_mx4_quantize_t(const float *X, uint8_t *Q, uint8_t *S, int R, int L,
@@ -301,7 +309,7 @@ MOE_GG_API int moe_gg_mx4_quantize_t(const float *X, uint8_t *Q, uint8_t *S, int
  * uses (source: the oarust page's expert_for_row).
  *
  *   expert_off int32 [E+1] (device), out int32 [M] (device).
- * Shapes: M, E >= 1 (EINVAL otherwise).
+ * Shapes: M >= 0, E >= 1 (EINVAL otherwise).
  */
 MOE_GG_API int moe_gg_row_experts(const int32_t *expert_off, int E, int M, int32_t *out,
                                   hipStream_t stream);

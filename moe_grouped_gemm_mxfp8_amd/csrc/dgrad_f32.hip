@@ -196,8 +196,11 @@ extern "C" MOE_GG_API int moe_gg_dgrad_f32(const float *A, const float *B, float
                                            const int32_t *expert_off, int M, int N, int K, int E,
                                            hipStream_t stream) {
   using namespace moe_gg;
-  if (!A || !B || !C || !expert_off) return MOE_GG_EINVAL;
-  if (M <= 0 || N <= 0 || K <= 0 || E <= 0) return MOE_GG_EINVAL;
+  if (M < 0 || N < 0 || K < 0 || E <= 0 || !expert_off) return MOE_GG_EINVAL;
+  if (M == 0 || K == 0) return MOE_GG_OK;                 // no output element
+  // an empty contraction (N = 0) writes zeros; g and W, then of zero size,
+  // are never read and may be null
+  if (!C || (N > 0 && (!A || !B))) return MOE_GG_EINVAL;
   if (K % 4 || N % 4) return MOE_GG_EUNSUPPORTED;
   if (const int st = check_offsets_if_asked(expert_off, E, M, stream)) return st;
   const dim3 grid((K + BK - 1) / BK, (M + BM - 1) / BM);
@@ -209,7 +212,9 @@ extern "C" MOE_GG_API int moe_gg_dgrad_f32(const float *A, const float *B, float
 extern "C" MOE_GG_API int moe_gg_row_experts(const int32_t *expert_off, int E, int M, int32_t *out,
                                              hipStream_t stream) {
   using namespace moe_gg;
-  if (!expert_off || !out || M <= 0 || E <= 0) return MOE_GG_EINVAL;
+  if (!expert_off || M < 0 || E <= 0) return MOE_GG_EINVAL;
+  if (M == 0) return MOE_GG_OK;
+  if (!out) return MOE_GG_EINVAL;
   const int threads = 256;
   hipLaunchKernelGGL(row_experts_kernel, dim3((M + threads - 1) / threads), dim3(threads), 0, stream,
                      expert_off, E, M, out);

@@ -268,7 +268,7 @@ __global__ __launch_bounds__(NTHREAD, 1) void grouped_mxfp8_kernel(
   };
 
   // ---- prologue: first step in flight ----
-  if (ld_t.kind == 1) {
+  if (ld_t.kind == 1 && nk > 0) {
     issue_stage(0);
     mark[0] = ops;
     advance();
@@ -319,8 +319,11 @@ __global__ __launch_bounds__(NTHREAD, 1) void grouped_mxfp8_kernel(
 int launch_grouped(bool split, bool xfp4, const uint8_t *A, const uint8_t *B, uint16_t *C, const uint8_t *scale_A,
                    const uint8_t *scale_B, const int32_t *expert_off, int M, int N, int K, int E,
                    hipStream_t stream) {
-  if (!A || !B || !C || !scale_A || !scale_B || !expert_off) return MOE_GG_EINVAL;
-  if (M <= 0 || N <= 0 || K <= 0 || E <= 0) return MOE_GG_EINVAL;
+  if (M < 0 || N < 0 || K < 0 || E <= 0 || !expert_off) return MOE_GG_EINVAL;
+  if (M == 0 || N == 0) return MOE_GG_OK;                 // no output element
+  // an empty contraction (K = 0) writes zeros; the operands, then of zero
+  // size, are never read and may be null
+  if (!C || (K > 0 && (!A || !B || !scale_A || !scale_B))) return MOE_GG_EINVAL;
   if (K % 32) return MOE_GG_EINVAL;
   if (N % TK || K % TT || E > MAX_E) return MOE_GG_EUNSUPPORTED;
   // 32-bit byte offsets inside one 256-row panel and inside a tile of C

@@ -278,7 +278,9 @@ __global__ __launch_bounds__(256) void mx_quantize_t_kernel(const float *__restr
 }
 
 int launch_quantize_t(int fmt, const float *X, uint8_t *Q, uint8_t *S, int R, int L, hipStream_t stream) {
-  if (!X || !Q || !S || R <= 0 || L <= 0 || R % 32) return MOE_GG_EINVAL;
+  if (R < 0 || L < 0) return MOE_GG_EINVAL;
+  if (R == 0 || L == 0) return MOE_GG_OK;                 // nothing to quantise
+  if (!X || !Q || !S || R % 32) return MOE_GG_EINVAL;
   if (L % 4) return MOE_GG_EUNSUPPORTED;
   const int tiles_t = (R + QT_TOK - 1) / QT_TOK, tiles_f = (L + QT_FEAT - 1) / QT_FEAT;
   const int64_t blocks = static_cast<int64_t>(tiles_t) * tiles_f;
@@ -296,7 +298,9 @@ int launch_quantize_t(int fmt, const float *X, uint8_t *Q, uint8_t *S, int R, in
 }
 
 int launch_quantize(bool roundup, const float *X, uint8_t *Q, uint8_t *S, int R, int L, hipStream_t stream) {
-  if (!X || !Q || !S || R <= 0 || L < 32 || L % 32) return MOE_GG_EINVAL;
+  if (R < 0 || L < 0) return MOE_GG_EINVAL;
+  if (R == 0 || L == 0) return MOE_GG_OK;                 // nothing to quantise
+  if (!X || !Q || !S || L % 32) return MOE_GG_EINVAL;
   const int64_t total = static_cast<int64_t>(R) * L;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return MOE_GG_ELAUNCH;
@@ -316,7 +320,9 @@ int launch_quantize(bool roundup, const float *X, uint8_t *Q, uint8_t *S, int R,
 }
 
 int launch_quantize4(const float *X, uint8_t *Q, uint8_t *S, int R, int L, hipStream_t stream) {
-  if (!X || !Q || !S || R <= 0 || L < 32 || L % 32) return MOE_GG_EINVAL;
+  if (R < 0 || L < 0) return MOE_GG_EINVAL;
+  if (R == 0 || L == 0) return MOE_GG_OK;                 // nothing to quantise
+  if (!X || !Q || !S || L % 32) return MOE_GG_EINVAL;
   const int64_t total = static_cast<int64_t>(R) * L;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return MOE_GG_ELAUNCH;

@@ -288,8 +288,11 @@ namespace {
 int launch_wgrad(bool split, const uint8_t *A, const uint8_t *B, uint16_t *C, const uint8_t *scale_A,
                  const uint8_t *scale_B, const int32_t *expert_off, int M, int N, int K, int E,
                  hipStream_t stream) {
-  if (!A || !B || !C || !scale_A || !scale_B || !expert_off) return MOE_GG_EINVAL;
-  if (M <= 0 || N <= 0 || K <= 0 || E <= 0) return MOE_GG_EINVAL;
+  if (M < 0 || N < 0 || K < 0 || E <= 0 || !expert_off) return MOE_GG_EINVAL;
+  if (N == 0 || K == 0) return MOE_GG_OK;                 // no output element
+  // no tokens (M = 0): every expert is empty and its rows are written +0.0;
+  // the operands, then of zero size, are never read and may be null
+  if (!C || (M > 0 && (!A || !B || !scale_A || !scale_B))) return MOE_GG_EINVAL;
   if (M % TT) return MOE_GG_EINVAL;
   if (N % TN || K % TK || E > MAX_EXPERTS) return MOE_GG_EUNSUPPORTED;
   // the buffer descriptors address one 256-row operand panel with 32-bit offsets

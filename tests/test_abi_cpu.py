@@ -64,7 +64,7 @@ def test_host_validation_wgrad(lib, name):
     ok = (256, 256, 256, 2)
     assert f(None, p, p, p, p, p, *ok, None) == -1
     assert f(p, p, p, p, p, None, *ok, None) == -1
-    assert f(p, p, p, p, p, p, 0, 256, 256, 2, None) == -1
+    assert f(p, p, p, p, p, p, -128, 256, 256, 2, None) == -1
     assert f(p, p, p, p, p, p, 256, 256, 256, 0, None) == -1
     assert f(p, p, p, p, p, p, 96, 256, 256, 2, None) == -1        # M % 128
     assert f(p, p, p, p, p, p, 256, 200, 256, 2, None) == -2       # N % 256
@@ -82,7 +82,7 @@ def test_host_validation_grouped(lib, name):
     ok = (300, 256, 256, 3)                                         # M need not be a tile multiple
     assert f(None, p, p, p, p, p, *ok, None) == -1
     assert f(p, p, p, p, p, None, *ok, None) == -1
-    assert f(p, p, p, p, p, p, 0, 256, 256, 3, None) == -1
+    assert f(p, p, p, p, p, p, -1, 256, 256, 3, None) == -1
     assert f(p, p, p, p, p, p, 300, 256, 256, 0, None) == -1
     assert f(p, p, p, p, p, p, 300, 256, 48, 3, None) == -1        # K % 32
     assert f(p, p, p, p, p, p, 300, 200, 256, 3, None) == -2       # N % 256
@@ -98,10 +98,10 @@ def test_host_validation_dgrad_quantize_rows(lib):
     assert lib.moe_gg_dgrad_f32(p, p, p, p, 8, 8, 6, 1, None) == -2
     assert lib.moe_gg_mx_quantize(p, p, None, 4, 64, None) == -1
     assert lib.moe_gg_mx_quantize(p, p, p, 4, 48, None) == -1
-    assert lib.moe_gg_mx_quantize(p, p, p, 0, 64, None) == -1
+    assert lib.moe_gg_mx_quantize(p, p, p, -4, 64, None) == -1
     assert lib.moe_gg_mx_quantize_t(p, p, None, 64, 8, None) == -1
     assert lib.moe_gg_mx_quantize_t(p, p, p, 48, 8, None) == -1      # R % 32
-    assert lib.moe_gg_mx_quantize_t(p, p, p, 64, 0, None) == -1
+    assert lib.moe_gg_mx_quantize_t(p, p, p, 64, -8, None) == -1
     assert lib.moe_gg_mx_quantize_t(p, p, p, 64, 6, None) == -2      # L % 4
     assert lib.moe_gg_mx_quantize_roundup(p, p, p, 4, 48, None) == -1
     assert lib.moe_gg_mx_quantize_roundup(None, p, p, 4, 64, None) == -1
@@ -109,12 +109,48 @@ def test_host_validation_dgrad_quantize_rows(lib):
     assert lib.moe_gg_mx_quantize_t_roundup(p, p, p, 64, 6, None) == -2
     assert lib.moe_gg_mx4_quantize(p, p, None, 4, 64, None) == -1
     assert lib.moe_gg_mx4_quantize(p, p, p, 4, 48, None) == -1
-    assert lib.moe_gg_mx4_quantize(p, p, p, 0, 64, None) == -1
+    assert lib.moe_gg_mx4_quantize(p, p, p, -4, 64, None) == -1
     assert lib.moe_gg_mx4_quantize_t(p, p, None, 64, 8, None) == -1
     assert lib.moe_gg_mx4_quantize_t(p, p, p, 48, 8, None) == -1     # R % 32
     assert lib.moe_gg_mx4_quantize_t(p, p, p, 64, 6, None) == -2     # L % 4
     assert lib.moe_gg_row_experts(p, 0, 10, p, None) == -1
     assert lib.moe_gg_row_experts(None, 2, 10, p, None) == -1
+
+
+def test_empty_outputs_return_ok_without_a_launch(lib):
+    """A call with no output element returns 0 before any HIP call (so also
+    here, without a GPU); pointers to zero-size buffers may be NULL, the
+    offsets may not; negative sizes stay invalid."""
+    p = ctypes.c_void_p(16)
+    for name in ("moe_gg_wgrad_mxfp8", "moe_gg_wgrad_mxfp8_fast"):
+        f = getattr(lib, name)
+        assert f(None, None, None, None, None, p, 256, 0, 256, 2, None) == 0       # N = 0
+        assert f(None, None, None, None, None, p, 256, 256, 0, 2, None) == 0       # K = 0
+        assert f(None, None, None, None, None, None, 256, 0, 256, 2, None) == -1   # offsets still required
+        assert f(None, None, None, None, None, p, 256, -256, 256, 2, None) == -1
+        assert f(p, p, None, p, p, p, 0, 256, 256, 2, None) == -1                  # M = 0 writes C: C required
+    for name in ("moe_gg_grouped_mxfp8", "moe_gg_grouped_mxfp8_fast", "moe_gg_grouped_a8w4",
+                 "moe_gg_grouped_a8w4_fast"):
+        f = getattr(lib, name)
+        assert f(None, None, None, None, None, p, 0, 256, 256, 3, None) == 0       # M = 0
+        assert f(None, None, None, None, None, p, 300, 0, 256, 3, None) == 0       # N = 0
+        assert f(None, None, None, None, None, None, 0, 256, 256, 3, None) == -1
+        assert f(p, p, p, p, p, p, 300, 256, -32, 3, None) == -1
+        assert f(None, None, None, None, None, p, 300, 256, 0, 3, None) == -1      # K = 0 writes C: C required
+    assert lib.moe_gg_dgrad_f32(None, None, None, p, 0, 8, 8, 1, None) == 0       # M = 0
+    assert lib.moe_gg_dgrad_f32(None, None, None, p, 8, 8, 0, 1, None) == 0       # K = 0
+    assert lib.moe_gg_dgrad_f32(None, None, None, None, 0, 8, 8, 1, None) == -1
+    assert lib.moe_gg_dgrad_f32(None, None, None, p, 8, 0, 8, 1, None) == -1      # N = 0 writes dx: dx required
+    for name in ("moe_gg_mx_quantize", "moe_gg_mx_quantize_roundup", "moe_gg_mx4_quantize",
+                 "moe_gg_mx_quantize_t", "moe_gg_mx_quantize_t_roundup", "moe_gg_mx4_quantize_t"):
+        f = getattr(lib, name)
+        assert f(None, None, None, 0, 64, None) == 0
+        assert f(None, None, None, 64, 0, None) == 0
+        assert f(None, None, None, 0, 0, None) == 0
+        assert f(None, None, None, -32, 64, None) == -1
+    assert lib.moe_gg_row_experts(p, 2, 0, None, None) == 0
+    assert lib.moe_gg_row_experts(p, 2, -1, p, None) == -1
+    assert lib.moe_gg_row_experts(None, 2, 0, None, None) == -1
 
 
 def test_python_binding_refuses_cpu_tensors():

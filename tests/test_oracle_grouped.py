@@ -316,3 +316,19 @@ def test_grouped_gemm_rows_match_the_whole_product():
     whole = oracle.grouped_gemm(ca, sa, cb, sb, off)
     rows = [0, 32, 33, 34, 79]
     assert np.array_equal(oracle.grouped_gemm_rows(ca, sa, cb, sb, off, rows), whole[rows])
+
+
+def test_oracle_empty_contractions_are_zero():
+    """The empty sum: no tokens (weight gradient), N = 0 (data gradient) and
+    K = 0 (grouped GEMM) give exact zeros of the output's shape."""
+    E, N, K = 3, 8, 16
+    z = np.zeros
+    got = oracle.wgrad(z((N, 0), np.uint8), z((N, 0), np.uint8), z((K, 0), np.uint8), z((K, 0), np.uint8),
+                       z(E + 1, np.int64))
+    assert got.shape == (E * N, K) and not np.any(got)
+    off = np.array([0, 2, 2, 5])
+    got = oracle.dgrad(z((5, 0), np.float32), z((3, 0, K), np.float32), off)
+    assert got.shape == (5, K) and not np.any(got)
+    got = oracle.grouped_gemm(z((5, 0), np.uint8), z((5, 0), np.uint8), z((3, 256, 0), np.uint8),
+                              z((3, 256, 0), np.uint8), off)
+    assert got.shape == (5, 256) and not np.any(got)
