@@ -29,7 +29,7 @@ int check_offsets_if_asked(const int32_t *off, int E, int M, hipStream_t stream)
 extern "C" MOE_GG_API const char *moe_gg_status_string(int status) {
   switch (status) {
     case MOE_GG_OK: return "ok";
-    case MOE_GG_EINVAL: return "invalid argument (null pointer, non-positive or misaligned size)";
+    case MOE_GG_EINVAL: return "invalid argument (null pointer, negative or misaligned size)";
     case MOE_GG_EUNSUPPORTED: return "unsupported shape for these kernels";
     case MOE_GG_ELAUNCH: return "kernel launch failed";
     default: return "unknown status";
