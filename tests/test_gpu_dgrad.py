@@ -30,6 +30,9 @@ CASES = {
     "long_n": (1000, 128, [129, 127]),
     # passes over 32-row blocks (0,3), (2,4), (0,2), (1,3), (2,3) of their tiles; a partial column tile
     "row_blocks": (160, 192, [70, 58, 40, 50, 38, 70, 20, 38]),
+    # boundaries 15, 16 and 17 rows into a 32-row block: leading and trailing 16-row half blocks,
+    # passes of a half block alone, a partial column tile
+    "half_blocks": (96, 160, [16, 31, 34, 31, 38, 20, 30]),
 }
 
 
