@@ -74,8 +74,8 @@ enum {
  *                        e4m3(A[n][m]) 2^(sA[n][m/32]-127) e4m3(B[k][m]) 2^(sB[k][m/32]-127) )
  *   accumulated in f32.
  *
- * Shapes: M, N, K >= 0, E >= 1; M % 128 == 0 (EINVAL otherwise; M = 0
- * writes +0.0 everywhere);
+ * Shapes: M, N, K >= 0, E >= 1, M % 32 == 0 (EINVAL otherwise; M = 0
+ * writes +0.0 everywhere); M % 128 == 0,
  * N % 256 == 0, K % 256 == 0, E <= 1024, 256 M < 2^32 and 512 K < 2^31
  * (EUNSUPPORTED otherwise: 32-bit offsets inside an operand panel and an
  * output tile).

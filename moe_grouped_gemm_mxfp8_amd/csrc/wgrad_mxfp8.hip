@@ -293,8 +293,10 @@ int launch_wgrad(bool split, const uint8_t *A, const uint8_t *B, uint16_t *C, co
   // no tokens (M = 0): every expert is empty and its rows are written +0.0;
   // the operands, then of zero size, are never read and may be null
   if (!C || (M > 0 && (!A || !B || !scale_A || !scale_B))) return MOE_GG_EINVAL;
-  if (M % TT) return MOE_GG_EINVAL;
-  if (N % TN || K % TK || E > MAX_EXPERTS) return MOE_GG_EUNSUPPORTED;
+  if (M % 32) return MOE_GG_EINVAL;                       // whole 32-token scale blocks
+  // the kernel steps through the tokens 128 at a time, with scale dwords of
+  // four blocks (rows of M/32 scale bytes stay 4-byte aligned)
+  if (M % TT || N % TN || K % TK || E > MAX_EXPERTS) return MOE_GG_EUNSUPPORTED;
   // the buffer descriptors address one 256-row operand panel with 32-bit offsets
   if (static_cast<uint64_t>(TK) * static_cast<uint64_t>(M) > 0xFFFFFFFFull) return MOE_GG_EUNSUPPORTED;
   // and one 256-row tile of the bf16 output (a signed 32-bit size)

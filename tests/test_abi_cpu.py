@@ -66,7 +66,8 @@ def test_host_validation_wgrad(lib, name):
     assert f(p, p, p, p, p, None, *ok, None) == -1
     assert f(p, p, p, p, p, p, -128, 256, 256, 2, None) == -1
     assert f(p, p, p, p, p, p, 256, 256, 256, 0, None) == -1
-    assert f(p, p, p, p, p, p, 96, 256, 256, 2, None) == -1        # M % 128
+    assert f(p, p, p, p, p, p, 80, 256, 256, 2, None) == -1        # M % 32: partial scale block
+    assert f(p, p, p, p, p, p, 96, 256, 256, 2, None) == -2        # M % 128: not tiled
     assert f(p, p, p, p, p, p, 256, 200, 256, 2, None) == -2       # N % 256
     assert f(p, p, p, p, p, p, 256, 256, 384, 2, None) == -2       # K % 256
     assert f(p, p, p, p, p, p, 256, 256, 256, 2000, None) == -2    # E above the ranking table
