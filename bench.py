@@ -155,6 +155,13 @@ def bench_wgrad(torch, mg, idx, steps, warmup, cpu_baseline, fast=False):
                      "algorithmic_bytes": algo_bytes, "algorithmic_flop": flop,
                      "hbm_gbs_algorithmic": round(algo_bytes / (ms * 1e-3) / 1e9, 1)},
     }
+    gbs = algo_bytes / (ms * 1e-3) / 1e9
+    if algo_bytes / (PEAK_HBM_GBS * 1e9) > flop / (PEAK_FP8_TFLOPS * 1e12):
+        # the bf16 output's stores outweigh the MFMA work (the aligned 2048^3 and
+        # the 64-expert workloads): the binding roofline is HBM
+        line["roofline"].update({"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                 "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                 "fp8_frac": round(tflops / PEAK_FP8_TFLOPS, 4)})
     if cpu_baseline:
         line["cpu_baseline"] = cpu_wgrad_baseline(inp)
     return line
