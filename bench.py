@@ -119,6 +119,18 @@ def time_steps(torch, fn, steps, warmup):
     return start.elapsed_time(stop) / steps  # ms per step
 
 
+def bind_roofline(line, flop, nbytes, ms):
+    """Switch a GEMM line's roofline to HBM when the algorithmic bytes take longer
+    at the HBM peak than the useful FLOP at the fp8 MFMA peak (the binding roofline
+    is the larger floor); the fp8 fraction stays beside it."""
+    if nbytes / (PEAK_HBM_GBS * 1e9) <= flop / (PEAK_FP8_TFLOPS * 1e12):
+        return
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    tf = flop / (ms * 1e-3) / 1e12
+    line["roofline"].update({"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                             "frac": round(gbs / PEAK_HBM_GBS, 4), "fp8_frac": round(tf / PEAK_FP8_TFLOPS, 4)})
+
+
 def bench_wgrad(torch, mg, idx, steps, warmup, cpu_baseline, fast=False):
     w = wl.WORKLOADS[idx]
     inp = wl.make_wgrad_inputs(idx)
@@ -155,13 +167,9 @@ def bench_wgrad(torch, mg, idx, steps, warmup, cpu_baseline, fast=False):
                      "algorithmic_bytes": algo_bytes, "algorithmic_flop": flop,
                      "hbm_gbs_algorithmic": round(algo_bytes / (ms * 1e-3) / 1e9, 1)},
     }
-    gbs = algo_bytes / (ms * 1e-3) / 1e9
-    if algo_bytes / (PEAK_HBM_GBS * 1e9) > flop / (PEAK_FP8_TFLOPS * 1e12):
-        # the bf16 output's stores outweigh the MFMA work (the aligned 2048^3 and
-        # the 64-expert workloads): the binding roofline is HBM
-        line["roofline"].update({"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                 "frac": round(gbs / PEAK_HBM_GBS, 4),
-                                 "fp8_frac": round(tflops / PEAK_FP8_TFLOPS, 4)})
+    # the aligned 2048^3 and the 64-expert workloads: the bf16 output's stores
+    # outweigh the MFMA work
+    bind_roofline(line, flop, algo_bytes, ms)
     if cpu_baseline:
         line["cpu_baseline"] = cpu_wgrad_baseline(inp)
     return line
@@ -251,6 +259,7 @@ def bench_grouped(torch, mg, idx, steps, warmup, cpu_baseline, fast=False):
                          "frac": round(tf / PEAK_FP8_TFLOPS, 4),
                          "traffic": None if fast else read_traffic("grouped", idx),
                          "algorithmic_bytes": int(nbytes), "algorithmic_flop": flop}}
+    bind_roofline(line, flop, nbytes, ms)
     if cpu_baseline:
         import oracle
         qa_h, sa_h = qa.cpu().numpy(), sa.cpu().numpy()
@@ -305,6 +314,7 @@ def bench_forward(torch, mg, idx, steps, warmup, cpu_baseline, fast=False, fp4=F
                          "frac": round(tf / PEAK_FP8_TFLOPS, 4),
                          "traffic": None if fast else read_traffic(name, idx),
                          "algorithmic_bytes": int(nbytes), "algorithmic_flop": flop}}
+    bind_roofline(line, flop, nbytes, ms)
     if cpu_baseline:
         import oracle
         rows = int(inp["off"][E // 8])                            # the tokens of the first E/8 experts
