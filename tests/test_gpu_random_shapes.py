@@ -1,0 +1,86 @@
+"""Seeded random shapes and expert offsets (empty experts, unaligned bounds,
+rows of several experts per tile) for the weight gradient, the data gradient,
+the grouped GEMM and the row map, each against the oracle at the usual bar."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from gpu_helpers import dev, host, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+SEEDS = list(range(8))
+
+
+def _counts(rng, E, M):
+    """M tokens over E experts, some of them empty, bounds anywhere."""
+    p = rng.random(E) * (rng.random(E) > 0.25)
+    if p.sum() == 0:
+        p[rng.integers(E)] = 1.0
+    return rng.multinomial(M, p / p.sum())
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_wgrad(seed):
+    torch, mg = require_gpu()
+    rng = np.random.default_rng(1000 + seed)
+    E = int(rng.integers(1, 7))
+    M = 128 * int(rng.integers(1, 9))
+    N, K = 256 * int(rng.integers(1, 3)), 256 * int(rng.integers(1, 3))
+    off = wl.offsets_from_counts(_counts(rng, E, M))
+    gT = rng.standard_normal((N, M)).astype(np.float32)
+    xT = rng.standard_normal((K, M)).astype(np.float32)
+    gT[rng.random(gT.shape) < 0.01] *= 64
+    xT[rng.random(xT.shape) < 0.01] *= 64
+    ca, sa = oracle.mx_quantize(gT)
+    cb, sb = oracle.mx_quantize(xT)
+    say("random wgrad", seed, E, M, N, K, off.tolist())
+    out = mg.wgrad_mxfp8(dev(torch, ca), dev(torch, cb), dev(torch, sa), dev(torch, sb), dev(torch, off))
+    torch.cuda.synchronize()
+    ref = oracle.wgrad(ca, sa, cb, sb, off)
+    got = host(out).astype(np.float64)
+    assert oracle.wgrad_excess(got, ref) <= 0
+    for e in np.flatnonzero(np.diff(off) == 0):
+        assert not np.any(got[e * N:(e + 1) * N])
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_dgrad_and_row_map(seed):
+    torch, mg = require_gpu()
+    rng = np.random.default_rng(2000 + seed)
+    E = int(rng.integers(1, 12))
+    M = int(rng.integers(1, 700))
+    N, K = 4 * int(rng.integers(1, 100)), 4 * int(rng.integers(1, 100))
+    off = wl.offsets_from_counts(_counts(rng, E, M))
+    g = rng.standard_normal((M, N)).astype(np.float32)
+    W = (rng.standard_normal((E, N, K)) / np.sqrt(N)).astype(np.float32)
+    say("random dgrad", seed, E, M, N, K, off.tolist())
+    off_d = dev(torch, off)
+    out = mg.dgrad_f32(dev(torch, g), dev(torch, W), off_d)
+    rows = mg.row_experts(off_d, M)
+    torch.cuda.synchronize()
+    ref = oracle.dgrad(g, W, off)
+    assert oracle.dgrad_ok(host(out).astype(np.float64), ref, N)
+    assert np.array_equal(host(rows), oracle.row_experts(off, M))
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_grouped(seed):
+    torch, mg = require_gpu()
+    rng = np.random.default_rng(3000 + seed)
+    E = int(rng.integers(1, 10))
+    M = int(rng.integers(1, 900))
+    N, K = 256 * int(rng.integers(1, 3)), 128 * int(rng.integers(1, 4))
+    off = wl.offsets_from_counts(_counts(rng, E, M))
+    a = rng.standard_normal((M, K)).astype(np.float32)
+    a[rng.random(a.shape) < 0.01] *= 64
+    b = rng.standard_normal((E * N, K)).astype(np.float32)
+    ca, sa = oracle.mx_quantize(a)
+    cb, sb = oracle.mx_quantize(b)
+    cb, sb = cb.reshape(E, N, K), sb.reshape(E, N, K // 32)
+    say("random grouped", seed, E, M, N, K, off.tolist())
+    out = mg.grouped_mxfp8(dev(torch, ca), dev(torch, cb), dev(torch, sa), dev(torch, sb), dev(torch, off))
+    torch.cuda.synchronize()
+    ref = oracle.grouped_gemm(ca, sa, cb, sb, off)
+    assert oracle.wgrad_excess(host(out).astype(np.float64), ref) <= 0
