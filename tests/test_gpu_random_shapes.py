@@ -84,3 +84,58 @@ def test_random_grouped(seed):
     torch.cuda.synchronize()
     ref = oracle.grouped_gemm(ca, sa, cb, sb, off)
     assert oracle.wgrad_excess(host(out).astype(np.float64), ref) <= 0
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_quantisers(seed):
+    """Row and transposing quantisers (both MXFP8 rules, MXFP4) on random shapes
+    with a wide dynamic range: codes and scales bit-exact against the oracle."""
+    torch, mg = require_gpu()
+    rng = np.random.default_rng(4000 + seed)
+    R, L = int(rng.integers(1, 300)), 32 * int(rng.integers(1, 20))
+    x = (rng.standard_normal((R, L)) * np.exp2(rng.integers(-20, 20, size=(R, L)))).astype(np.float32)
+    x[rng.random(x.shape) < 0.05] = 0.0
+    say("random quantisers", seed, R, L)
+    xd = dev(torch, x)
+    for rule in ("floor", "roundup"):
+        q, s = mg.mx_quantize(xd, rule=rule)
+        cq, cs = oracle.mx_quantize(x, rule=rule)
+        assert np.array_equal(host(q), cq) and np.array_equal(host(s), cs), rule
+    q, s = mg.mx4_quantize(xd)
+    cq, cs = oracle.mx4_quantize(x)
+    assert np.array_equal(host(q), cq) and np.array_equal(host(s), cs), "mx4"
+    # the transposing forms quantise x^T along R: R a multiple of 32, L of 4
+    Rt, Lt = 32 * int(rng.integers(1, 12)), 4 * int(rng.integers(1, 80))
+    y = (rng.standard_normal((Rt, Lt)) * np.exp2(rng.integers(-20, 20, size=(Rt, Lt)))).astype(np.float32)
+    yd = dev(torch, y)
+    yt = np.ascontiguousarray(y.T)
+    for rule in ("floor", "roundup"):
+        q, s = mg.mx_quantize_t(yd, rule=rule)
+        cq, cs = oracle.mx_quantize(yt, rule=rule)
+        assert np.array_equal(host(q), cq) and np.array_equal(host(s), cs), ("t", rule)
+    q, s = mg.mx4_quantize_t(yd)
+    cq, cs = oracle.mx4_quantize(yt)
+    assert np.array_equal(host(q), cq) and np.array_equal(host(s), cs), "mx4_t"
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_a8w4(seed):
+    torch, mg = require_gpu()
+    rng = np.random.default_rng(5000 + seed)
+    E = int(rng.integers(1, 10))
+    M = int(rng.integers(1, 900))
+    N, K = 256 * int(rng.integers(1, 3)), 128 * int(rng.integers(1, 4))
+    off = wl.offsets_from_counts(_counts(rng, E, M))
+    a = rng.standard_normal((M, K)).astype(np.float32)
+    a[rng.random(a.shape) < 0.01] *= 64
+    b = rng.standard_normal((E * N, K)).astype(np.float32)
+    ca, sa = oracle.mx_quantize(a)
+    cb, sb = oracle.mx4_quantize(b)
+    cb, sb = cb.reshape(E, N, K // 2), sb.reshape(E, N, K // 32)
+    say("random a8w4", seed, E, M, N, K, off.tolist())
+    out = mg.grouped_mxfp8(dev(torch, ca), dev(torch, cb), dev(torch, sa), dev(torch, sb), dev(torch, off),
+                           b_fp4=True)
+    torch.cuda.synchronize()
+    ref = oracle.grouped_gemm(ca, sa, cb, sb, off, b_format="e2m1")
+    assert oracle.wgrad_excess(host(out).astype(np.float64), ref) <= 0
