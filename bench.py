@@ -34,6 +34,7 @@ import workloads as wl  # noqa: E402
 
 # MI355X published dense peaks (per GPU)
 PEAK_FP8_TFLOPS = 5000.0
+PEAK_BF16_TFLOPS = 2500.0
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 
@@ -156,14 +157,16 @@ def bench_wgrad(torch, mg, idx, steps, warmup, cpu_baseline, fast=False):
         "unit": "TFLOP/s",
         "pct_of_fp8_peak": round(100.0 * tflops / PEAK_FP8_TFLOPS, 2),
         "ms_per_step": round(ms, 4),
-        "dtype": "fp8e4m3*fp8e4m3->f32 acc, bf16 out",
-        "mode": "single block-scaled MFMA pass (hardware run-of-8 rounding)" if fast
-        else "two block-scaled MFMA passes (g^T codes >= 128 / the rest); within the exact-sum tolerance",
+        "dtype": "fp8e4m3*fp8e4m3->f32 acc, bf16 out" if fast else "mxfp8 (e4m3+e8m0) -> bf16 MFMA, f32 acc, bf16 out",
+        "mode": "block-scaled fp8 MFMA (hardware run-of-8 rounding)" if fast
+        else "E4M3 x E8M0 converted exactly to bf16, bf16 MFMA (exact-sum accuracy)",
         "config": {"workload": w.name, "E": w.E, "M": w.M, "N": w.N, "K": w.K,
                    "tokens_per_expert": [int(c) for c in np.diff(off_np)]},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_FP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP8_TFLOPS, 4),
                      "traffic": None if fast else read_traffic("wgrad", idx),
+                     "mfma": "v_mfma_scale_f32_32x32x64_f8f6f4 (fp8)" if fast else "v_mfma_f32_32x32x16_bf16",
+                     "frac_of_mfma_dtype_peak": round(tflops / (PEAK_FP8_TFLOPS if fast else PEAK_BF16_TFLOPS), 4),
                      "algorithmic_bytes": algo_bytes, "algorithmic_flop": flop,
                      "hbm_gbs_algorithmic": round(algo_bytes / (ms * 1e-3) / 1e9, 1)},
     }

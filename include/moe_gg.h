@@ -88,12 +88,16 @@ enum {
  * Accuracy: gfx950's block-scaled fp8 MFMA sums each run of 8 consecutive
  * tokens after truncating every product toward zero to a multiple of
  * 2^(floor(log2 p_max) - 13), p_max the largest product magnitude of the run
- * (measured on the hardware; runs are then added exactly, the accumulator in
- * f32).  A run whose products span more than 2^6 loses low bits.  This entry
- * point therefore multiplies in two passes, the g^T codes of magnitude >= 128
- * and the rest, so that no run mixes a block's largest codes with its small
- * ones; the result stays within 2^-7 |ref| + 2^-12 rms(ref) of the exact sum
- * also for blocks with 64x outliers.  Twice the MFMA work of one pass.
+ * (measured on the hardware).  Where an outlier of g^T meets an outlier of
+ * x^T at one token, that run's other products are mostly lost, and no split
+ * of the codes into two passes avoids it (several outliers of one row can
+ * share a run).  This entry point therefore converts the codes, times their
+ * scales, to bf16 (exactly: 4 significant bits, the scale inside bf16's
+ * exponent range) and multiplies them on the bf16 MFMA, which adds its
+ * products without that truncation; the accumulator is f32.  The result is
+ * the exact sum up to f32 accumulation and the final bf16 rounding, on any
+ * input.  Scale bytes below 2^-126 relative to the codes' range (results
+ * below bf16's normal range) are flushed by the conversion.
  */
 MOE_GG_API int moe_gg_wgrad_mxfp8(const uint8_t *A, const uint8_t *B, uint16_t *C,
                                   const uint8_t *scale_A, const uint8_t *scale_B,
@@ -101,13 +105,14 @@ MOE_GG_API int moe_gg_wgrad_mxfp8(const uint8_t *A, const uint8_t *B, uint16_t *
                                   hipStream_t stream);
 
 /*
- * The same grouped MXFP8 weight gradient in ONE block-scaled MFMA pass: the
- * hardware's own reduction as described above, half the MFMA work.  Same
- * arguments, layouts, shapes and status codes as moe_gg_wgrad_mxfp8.  The
- * result equals the exact sum when every 8-token run's products are within
- * 2^6 of each other, and otherwise can differ by up to 2^-13 of the run's
- * largest product per product.  For callers whose inputs have a moderate
- * in-block range (no outliers) or who accept the hardware's rounding.
+ * The same grouped MXFP8 weight gradient on the block-scaled fp8 MFMA
+ * (v_mfma_scale_f32_32x32x64_f8f6f4): the hardware's own reduction as
+ * described above, at twice the bf16 MFMA's rate.  Same arguments, layouts,
+ * shapes and status codes as moe_gg_wgrad_mxfp8.  The result equals the
+ * exact sum when every 8-token run's products are within 2^6 of each other,
+ * and otherwise can differ by up to 2^-13 of the run's largest product per
+ * product.  For callers whose inputs have a moderate in-block range (no
+ * outliers) or who accept the hardware's rounding.
  */
 MOE_GG_API int moe_gg_wgrad_mxfp8_fast(const uint8_t *A, const uint8_t *B, uint16_t *C,
                                        const uint8_t *scale_A, const uint8_t *scale_B,

@@ -13,6 +13,7 @@ int check_offsets_if_asked(const int32_t *off, int E, int M, hipStream_t stream)
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
@@ -39,13 +40,21 @@ __device__ __forceinline__ v4i make_srd(const void *base, uint32_t num_bytes) {
 // srd.base + voff + soff land at LDS byte lds_base + 16*i (or 4*i).  Issued as
 // inline asm so that the compiler's conservative LDS-DMA alias waits do not
 // serialise the double buffer; completion is tracked with vmcnt by the caller.
+// The LDS address comes from m0, a register the compiler reserves for itself:
+// the statement saves m0, sets it, waits the one wait state an m0 write needs
+// before an LDS-DMA load reads it, issues the load and puts m0 back, so no
+// value the compiler keeps in m0 is disturbed.
 __device__ __forceinline__ void dma_b128(v4i srd, uint32_t voff, uint32_t soff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
-               :: "v"(voff), "s"(srd), "s"(soff), "s"(lds_base) : "memory");
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %4\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds\n\t"
+               "s_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(voff), "s"(srd), "s"(soff), "s"(lds_base) : "memory");
 }
 __device__ __forceinline__ void dma_b32(v4i srd, uint32_t voff, uint32_t soff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dword %0, %1, %2 offen lds"
-               :: "v"(voff), "s"(srd), "s"(soff), "s"(lds_base) : "memory");
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %4\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds\n\t"
+               "s_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(voff), "s"(srd), "s"(soff), "s"(lds_base) : "memory");
 }
 
 template <int N>

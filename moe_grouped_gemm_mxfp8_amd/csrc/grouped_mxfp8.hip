@@ -85,7 +85,7 @@ __global__ __launch_bounds__(NTHREAD, 1) void grouped_mxfp8_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tilesJ = N / TK;
+  const int tilesJ = N / TA;
   const int nk = K / TT;                   // contraction steps per tile
   const int G = gridDim.x;
 
@@ -116,7 +116,7 @@ __global__ __launch_bounds__(NTHREAD, 1) void grouped_mxfp8_kernel(
 #pragma unroll
     for (int j = 0; j < SCAN_PER; ++j) {
       const int e = e0 + j;
-      v[j] = e < E ? (s_row[e + 1] - s_row[e] + TN - 1) / TN : 0;
+      v[j] = e < E ? (s_row[e + 1] - s_row[e] + TB - 1) / TB : 0;
       cnt += v[j];
     }
     incl = block_scan<false>(cnt, red, tid);
@@ -130,8 +130,8 @@ __global__ __launch_bounds__(NTHREAD, 1) void grouped_mxfp8_kernel(
   }
   const int R = s_pre[E];                                  // expert row tiles
   const int row_first = s_row[0], row_end = s_row[E];
-  const int Zh = (row_first + TN - 1) / TN;                // row tiles of no expert before / after
-  const int Zt = (M - row_end + TN - 1) / TN;
+  const int Zh = (row_first + TB - 1) / TB;                // row tiles of no expert before / after
+  const int Zt = (M - row_end + TB - 1) / TB;
   const int expert_tiles = R * tilesJ;
   const int total = (R + Zh + Zt) * tilesJ;
 
@@ -154,14 +154,14 @@ __global__ __launch_bounds__(NTHREAD, 1) void grouped_mxfp8_kernel(
       const int r = o - s_pre[lo] * tilesJ;
       const int jt = r / ce, i = r - jt * ce;
       t.kind = 1; t.e = lo; t.jt = jt;
-      t.m0 = s_row[lo] + i * TN;
-      t.rows = min(TN, s_row[lo + 1] - t.m0);
+      t.m0 = s_row[lo] + i * TB;
+      t.rows = min(TB, s_row[lo + 1] - t.m0);
     } else {
       const int z = o - expert_tiles;
       const int zr = z / tilesJ;
       t.kind = 2; t.jt = z - zr * tilesJ;
-      if (zr < Zh) { t.m0 = zr * TN; t.rows = min(TN, row_first - t.m0); }
-      else { t.m0 = row_end + (zr - Zh) * TN; t.rows = min(TN, M - t.m0); }
+      if (zr < Zh) { t.m0 = zr * TB; t.rows = min(TB, row_first - t.m0); }
+      else { t.m0 = row_end + (zr - Zh) * TB; t.rows = min(TB, M - t.m0); }
     }
     return t;
   };
@@ -202,9 +202,9 @@ __global__ __launch_bounds__(NTHREAD, 1) void grouped_mxfp8_kernel(
   uint32_t xrow[4], grow[2];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
-    xrow[a] = ST_X + (XFP4 ? tile_row4(wk * 128 + a * 32 + l32) : tile_row(wk * 128 + a * 32 + l32));
+    xrow[a] = ST_A + (XFP4 ? tile_row4(wk * 128 + a * 32 + l32) : tile_row(wk * 128 + a * 32 + l32));
 #pragma unroll
-  for (int bb = 0; bb < 2; ++bb) grow[bb] = ST_G + tile_row(wn * 64 + bb * 32 + l32);
+  for (int bb = 0; bb < 2; ++bb) grow[bb] = ST_B + tile_row(wn * 64 + bb * 32 + l32);
   uint32_t chunk_off[2][2];   // [half][piece] -> 16-byte chunk offset within the row
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -229,27 +229,27 @@ __global__ __launch_bounds__(NTHREAD, 1) void grouped_mxfp8_kernel(
   auto issue_stage = [&](uint32_t buf) __attribute__((always_inline)) {
     if (!loader) return;
     const uint32_t cpos = static_cast<uint32_t>(ld_s * TT);
-    const size_t wrow = static_cast<size_t>(ld_t.e) * N + static_cast<size_t>(ld_t.jt) * TK;   // first weight row
+    const size_t wrow = static_cast<size_t>(ld_t.e) * N + static_cast<size_t>(ld_t.jt) * TA;   // first weight row
     const uint32_t rows = static_cast<uint32_t>(ld_t.rows);
-    const v4i srd_x = make_srd(B + wrow * Kx, TK * Kx);
+    const v4i srd_x = make_srd(B + wrow * Kx, TA * Kx);
     const v4i srd_g = make_srd(A + static_cast<size_t>(ld_t.m0) * K, rows * Kb);
     const uint32_t base = smem_base + buf * STAGE_BYTES;
     if constexpr (XFP4) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        dma_b128(srd_x, voff_x4[i], cpos / 2, __builtin_amdgcn_readfirstlane(base + ST_X + (w4 * 4 + i) * BLK4));
+        dma_b128(srd_x, voff_x4[i], cpos / 2, __builtin_amdgcn_readfirstlane(base + ST_A + (w4 * 4 + i) * BLK4));
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        dma_b128(srd_x, voff_t[i], cpos, __builtin_amdgcn_readfirstlane(base + ST_X + (w4 * 8 + i) * BLK));
+        dma_b128(srd_x, voff_t[i], cpos, __builtin_amdgcn_readfirstlane(base + ST_A + (w4 * 8 + i) * BLK));
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      dma_b128(srd_g, voff_t[i], cpos, __builtin_amdgcn_readfirstlane(base + ST_G + (w4 * 8 + i) * BLK));
+      dma_b128(srd_g, voff_t[i], cpos, __builtin_amdgcn_readfirstlane(base + ST_B + (w4 * 8 + i) * BLK));
     const v4i srd_sx = make_srd(SB + wrow * scale_row, 256u * scale_row);
     const v4i srd_sg = make_srd(SA + static_cast<size_t>(ld_t.m0) * scale_row, rows * scale_row);
-    dma_b32(srd_sx, voff_s, cpos / 32, __builtin_amdgcn_readfirstlane(base + ST_SX + w4 * 256));
-    dma_b32(srd_sg, voff_s, cpos / 32, __builtin_amdgcn_readfirstlane(base + ST_SG + w4 * 256));
+    dma_b32(srd_sx, voff_s, cpos / 32, __builtin_amdgcn_readfirstlane(base + ST_SA + w4 * 256));
+    dma_b32(srd_sg, voff_s, cpos / 32, __builtin_amdgcn_readfirstlane(base + ST_SB + w4 * 256));
     ops += LOADS_PER_STEP;
   };
   // wait until the loads of the step in buffer b have landed: every vector
@@ -282,8 +282,8 @@ __global__ __launch_bounds__(NTHREAD, 1) void grouped_mxfp8_kernel(
     const Tile cur = tile_of(lb + k * G);
     if (cur.kind == 0) break;
     const __amdgpu_buffer_rsrc_t crsrc = __builtin_amdgcn_make_buffer_rsrc(
-        C + static_cast<size_t>(cur.m0) * N + static_cast<size_t>(cur.jt) * TK, static_cast<short>(0),
-        static_cast<int>((static_cast<uint32_t>(cur.rows - 1) * Nu + TK) * 2u), 0x00020000);
+        C + static_cast<size_t>(cur.m0) * N + static_cast<size_t>(cur.jt) * TA, static_cast<short>(0),
+        static_cast<int>((static_cast<uint32_t>(cur.rows - 1) * Nu + TA) * 2u), 0x00020000);
     if (cur.kind == 2) {                                  // rows of no expert: +0.0
       store_zero_tile(crsrc, Nu, tid);
       ops += STORES_PER_TILE;
@@ -305,7 +305,7 @@ __global__ __launch_bounds__(NTHREAD, 1) void grouped_mxfp8_kernel(
         advance();
       }
       const uint8_t *st = smem + buf * STAGE_BYTES;
-      compute_step<SPLIT, XFP4>(st, acc, xrow, grow, chunk_off, wk, wn, l32, g, 0, TT, 0, TN);
+      compute_step<SPLIT, XFP4>(st, acc, xrow, grow, chunk_off, wk, wn, l32, g, 0, TT, 0, TB);
       buf ^= 1;
     }
     // ---- epilogue: C[m0 + m][j0 + j] for the tile's rows; the descriptor
@@ -325,17 +325,17 @@ int launch_grouped(bool split, bool xfp4, const uint8_t *A, const uint8_t *B, ui
   // size, are never read and may be null
   if (!C || (K > 0 && (!A || !B || !scale_A || !scale_B))) return MOE_GG_EINVAL;
   if (K % 32) return MOE_GG_EINVAL;
-  if (N % TK || K % TT || E > MAX_E) return MOE_GG_EUNSUPPORTED;
+  if (N % TA || K % TT || E > MAX_E) return MOE_GG_EUNSUPPORTED;
   // 32-bit byte offsets inside one 256-row panel and inside a tile of C
-  if (static_cast<uint64_t>(TN) * static_cast<uint64_t>(K) > 0xFFFFFFFFull) return MOE_GG_EUNSUPPORTED;
-  if (static_cast<uint64_t>(TN) * static_cast<uint64_t>(N) * 2u > 0x7FFFFFFFull) return MOE_GG_EUNSUPPORTED;
+  if (static_cast<uint64_t>(TB) * static_cast<uint64_t>(K) > 0xFFFFFFFFull) return MOE_GG_EUNSUPPORTED;
+  if (static_cast<uint64_t>(TB) * static_cast<uint64_t>(N) * 2u > 0x7FFFFFFFull) return MOE_GG_EUNSUPPORTED;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return MOE_GG_ELAUNCH;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     return MOE_GG_ELAUNCH;
   // row tiles: at most one partial tile per expert beyond ceil(M / 256), plus
   // the rows of no expert before and after
-  const int64_t total = (static_cast<int64_t>((M + TN - 1) / TN) + E + 2) * (N / TK);
+  const int64_t total = (static_cast<int64_t>((M + TB - 1) / TB) + E + 2) * (N / TA);
   if (total > 0x7FFFFFFF) return MOE_GG_EUNSUPPORTED;
   if (const int st = check_offsets_if_asked(expert_off, E, M, stream)) return st;
   const int grid = static_cast<int>(total < cus ? total : cus);

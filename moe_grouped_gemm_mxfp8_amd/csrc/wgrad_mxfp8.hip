@@ -27,9 +27,20 @@
 //    block, eight lanes per row reading the row's 128 bytes in order (whole
 //    lines, no permuted lanes), and rows are placed so that the 16 rows an
 //    MFMA operand read touches at once fall on 16 distinct bank groups.
-//  * 8 waves as 2 (k) x 4 (n); each wave owns a 128 x 64 output patch as
-//    4 x 2 accumulators of v_mfma_scale_f32_32x32x64_f8f6f4.  x^T is the
-//    MFMA A operand (rows = k) and g^T the B operand (columns = n).
+//  * 8 waves as 2 (k) x 4 (n); each wave owns a 128 (k) x 64 (n) output
+//    patch as 4 x 2 accumulators of 32 x 32 MFMA results.  x^T is the MFMA A
+//    operand (rows = k) and g^T the B operand (columns = n).
+//  * Exact form (the default entry point): the block-scaled fp8 MFMA
+//    truncates the products of every run of 8 tokens to 2^(largest exponent
+//    sum - 13), so where an outlier of g meets an outlier of x at one token
+//    the run's other products are lost (errors of ~1 against a bound of ~0.3
+//    on the 8192^3 workload, whichever codes are split into separate passes:
+//    several outliers of one row can share a run).  The default entry point
+//    therefore converts the staged E4M3 codes, times their E8M0 scales, to
+//    bf16 (exact) and multiplies on the bf16 MFMA, whose sums carry no such
+//    truncation (compute_step_bf16 in mx_gemm_core.hpp).  The single fp8
+//    pass (v_mfma_scale_f32_32x32x64_f8f6f4) stays available as the fast
+//    entry point, whose results follow the hardware's rounding.
 //  * Operand lane layout of the scaled MFMA (measured on gfx950, the decode
 //    page's lds_b8 note says the same for 16x16x128): lane l holds row l%32;
 //    lane group g = l/32 holds tokens 16g..16g+15 and 32+16g..32+16g+15 of the
@@ -38,8 +49,8 @@
 //    dword (scales are row-major [rows][M/32]); shifted right by 8g it serves
 //    both halves through op_sel = 0 and 2.
 //  * Epilogue: the bf16 tile goes through LDS (the buffer the tile's last
-//    step has freed) so that each store instruction writes whole 512-byte row
-//    segments; partial-line non-temporal stores measured several times slower.
+//    step has freed) so that each store instruction writes whole 128-byte row
+//    pieces; partial-line non-temporal stores measured several times slower.
 //    The stores drain while the next tile's steps run.
 #include "common.hpp"
 #include "mx_gemm_core.hpp"
@@ -107,7 +118,7 @@ struct Cursor {
   Tile ti;
 };
 
-template <bool SPLIT>
+template <bool EXACT>
 __global__ __launch_bounds__(NTHREAD, 1) void wgrad_mxfp8_kernel(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, uint16_t *__restrict__ C,
     const uint8_t *__restrict__ SA, const uint8_t *__restrict__ SB,
@@ -118,7 +129,7 @@ __global__ __launch_bounds__(NTHREAD, 1) void wgrad_mxfp8_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tilesN = N / TN, tilesK = K / TK;
+  const int tilesN = N / TB, tilesK = K / TA;     // x^T rows are the A operand, g^T rows the B operand
   const int T = tilesN * tilesK;
   const int total = E * T;
   const int G = gridDim.x;
@@ -165,14 +176,15 @@ __global__ __launch_bounds__(NTHREAD, 1) void wgrad_mxfp8_kernel(
   }
   const uint32_t voff_s = static_cast<uint32_t>(w4 * 64 + lane) * scale_row;
 
-  // MFMA operand addressing
+  // MFMA operand addressing: wave (wk, wn) owns grad_w columns wk*128 .. +127
+  // (k, A operand) and rows wn*64 .. +63 (n, B operand) of the tile
   const int wk = wave >> 2, wn = wave & 3;
   const int g = lane >> 5, l32 = lane & 31;
   uint32_t xrow[4], grow[2];
 #pragma unroll
-  for (int a = 0; a < 4; ++a) xrow[a] = ST_X + tile_row(wk * 128 + a * 32 + l32);
+  for (int a = 0; a < 4; ++a) xrow[a] = ST_A + tile_row(wk * 128 + a * 32 + l32);
 #pragma unroll
-  for (int b = 0; b < 2; ++b) grow[b] = ST_G + tile_row(wn * 64 + b * 32 + l32);
+  for (int b = 0; b < 2; ++b) grow[b] = ST_B + tile_row(wn * 64 + b * 32 + l32);
   uint32_t chunk_off[2][2];   // [half][piece] -> 16-byte chunk offset within the row
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -203,19 +215,19 @@ __global__ __launch_bounds__(NTHREAD, 1) void wgrad_mxfp8_kernel(
     if (!loader) return;
     const Tile &ti = c.ti;
     const uint32_t tok = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(ti.tok0 + c.s * TT));
-    const v4i srd_x = make_srd(B + static_cast<size_t>(ti.kt) * TK * M, TK * Mb);
-    const v4i srd_g = make_srd(A + static_cast<size_t>(ti.nt) * TN * M, TN * Mb);
+    const v4i srd_x = make_srd(B + static_cast<size_t>(ti.kt) * TA * M, TA * Mb);
+    const v4i srd_g = make_srd(A + static_cast<size_t>(ti.nt) * TB * M, TB * Mb);
     const uint32_t base = smem_base + buf * STAGE_BYTES;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      dma_b128(srd_x, voff_t[i], tok, __builtin_amdgcn_readfirstlane(base + ST_X + (w4 * 8 + i) * BLK));
+      dma_b128(srd_x, voff_t[i], tok, __builtin_amdgcn_readfirstlane(base + ST_A + (w4 * 8 + i) * BLK));
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      dma_b128(srd_g, voff_t[i], tok, __builtin_amdgcn_readfirstlane(base + ST_G + (w4 * 8 + i) * BLK));
-    const v4i srd_sx = make_srd(SB + static_cast<size_t>(ti.kt) * TK * scale_row, 256u * scale_row);
-    const v4i srd_sg = make_srd(SA + static_cast<size_t>(ti.nt) * TN * scale_row, 256u * scale_row);
-    dma_b32(srd_sx, voff_s, tok / 32, __builtin_amdgcn_readfirstlane(base + ST_SX + w4 * 256));
-    dma_b32(srd_sg, voff_s, tok / 32, __builtin_amdgcn_readfirstlane(base + ST_SG + w4 * 256));
+      dma_b128(srd_g, voff_t[i], tok, __builtin_amdgcn_readfirstlane(base + ST_B + (w4 * 8 + i) * BLK));
+    const v4i srd_sx = make_srd(SB + static_cast<size_t>(ti.kt) * TA * scale_row, 256u * scale_row);
+    const v4i srd_sg = make_srd(SA + static_cast<size_t>(ti.nt) * TB * scale_row, 256u * scale_row);
+    dma_b32(srd_sx, voff_s, tok / 32, __builtin_amdgcn_readfirstlane(base + ST_SA + w4 * 256));
+    dma_b32(srd_sg, voff_s, tok / 32, __builtin_amdgcn_readfirstlane(base + ST_SB + w4 * 256));
     ops += LOADS_PER_STEP;
   };
   // wait until the loads of the step in buffer b have landed: every vector
@@ -262,7 +274,10 @@ __global__ __launch_bounds__(NTHREAD, 1) void wgrad_mxfp8_kernel(
       }
 
       const uint8_t *st = smem + buf * STAGE_BYTES;
-      compute_step<SPLIT>(st, acc, xrow, grow, chunk_off, wk, wn, l32, g, cur.lo - s * TT, cur.hi - s * TT, 0, TN);
+      if constexpr (EXACT)
+        compute_step_bf16(st, acc, xrow, grow, wk, wn, l32, g, cur.lo - s * TT, cur.hi - s * TT);
+      else
+        compute_step<false>(st, acc, xrow, grow, chunk_off, wk, wn, l32, g, cur.lo - s * TT, cur.hi - s * TT, 0, TB);
       buf ^= 1;
     }
 
@@ -271,8 +286,8 @@ __global__ __launch_bounds__(NTHREAD, 1) void wgrad_mxfp8_kernel(
     // through a buffer descriptor with 32-bit byte offsets (non-temporal)
     const uint32_t Ku = static_cast<uint32_t>(K);
     const __amdgpu_buffer_rsrc_t crsrc = __builtin_amdgcn_make_buffer_rsrc(
-        C + (static_cast<size_t>(cur.e) * N + static_cast<size_t>(cur.nt) * TN) * K + static_cast<size_t>(cur.kt) * TK,
-        static_cast<short>(0), static_cast<int>(TN * Ku * 2u), 0x00020000);
+        C + (static_cast<size_t>(cur.e) * N + static_cast<size_t>(cur.nt) * TB) * K + static_cast<size_t>(cur.kt) * TA,
+        static_cast<short>(0), static_cast<int>(TB * Ku * 2u), 0x00020000);
     if (cur.nk == 0) store_zero_tile(crsrc, Ku, tid);     // empty expert: +0.0 everywhere
     else store_tile(acc, smem + (buf ^ 1) * STAGE_BYTES, crsrc, Ku, wk, wn, tid);
     ops += STORES_PER_TILE;
@@ -285,7 +300,7 @@ __global__ __launch_bounds__(NTHREAD, 1) void wgrad_mxfp8_kernel(
 
 namespace moe_gg {
 namespace {
-int launch_wgrad(bool split, const uint8_t *A, const uint8_t *B, uint16_t *C, const uint8_t *scale_A,
+int launch_wgrad(bool exact, const uint8_t *A, const uint8_t *B, uint16_t *C, const uint8_t *scale_A,
                  const uint8_t *scale_B, const int32_t *expert_off, int M, int N, int K, int E,
                  hipStream_t stream) {
   if (M < 0 || N < 0 || K < 0 || E <= 0 || !expert_off) return MOE_GG_EINVAL;
@@ -296,20 +311,20 @@ int launch_wgrad(bool split, const uint8_t *A, const uint8_t *B, uint16_t *C, co
   if (M % 32) return MOE_GG_EINVAL;                       // whole 32-token scale blocks
   // the kernel steps through the tokens 128 at a time, with scale dwords of
   // four blocks (rows of M/32 scale bytes stay 4-byte aligned)
-  if (M % TT || N % TN || K % TK || E > MAX_EXPERTS) return MOE_GG_EUNSUPPORTED;
+  if (M % TT || N % TB || K % TA || E > MAX_EXPERTS) return MOE_GG_EUNSUPPORTED;
   // the buffer descriptors address one 256-row operand panel with 32-bit offsets
-  if (static_cast<uint64_t>(TK) * static_cast<uint64_t>(M) > 0xFFFFFFFFull) return MOE_GG_EUNSUPPORTED;
+  if (static_cast<uint64_t>(TA) * static_cast<uint64_t>(M) > 0xFFFFFFFFull) return MOE_GG_EUNSUPPORTED;
   // and one 256-row tile of the bf16 output (a signed 32-bit size)
-  if (static_cast<uint64_t>(TN) * static_cast<uint64_t>(K) * 2u > 0x7FFFFFFFull) return MOE_GG_EUNSUPPORTED;
+  if (static_cast<uint64_t>(TB) * static_cast<uint64_t>(K) * 2u > 0x7FFFFFFFull) return MOE_GG_EUNSUPPORTED;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return MOE_GG_ELAUNCH;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     return MOE_GG_ELAUNCH;
-  const int64_t total = static_cast<int64_t>(E) * (N / TN) * (K / TK);
+  const int64_t total = static_cast<int64_t>(E) * (N / TB) * (K / TA);
   if (total > 0x7FFFFFFF) return MOE_GG_EUNSUPPORTED;
   if (const int st = check_offsets_if_asked(expert_off, E, M, stream)) return st;
   const int grid = static_cast<int>(total < cus ? total : cus);
-  if (split)
+  if (exact)
     hipLaunchKernelGGL(wgrad_mxfp8_kernel<true>, dim3(grid), dim3(NTHREAD), 0, stream, A, B, C, scale_A,
                        scale_B, expert_off, M, N, K, E);
   else

@@ -32,8 +32,9 @@ _U8 = (torch.uint8, torch.float8_e4m3fn, torch.float8_e8m0fnu) if hasattr(torch,
 def wgrad_mxfp8(a, b, scale_a, scale_b, expert_off, out=None, fast=False):
     """grad_w[E*N, K] (bf16) from g^T codes a[N, M], x^T codes b[K, M], E8M0 scales [.., M/32].
 
-    fast=False: two MFMA passes, within 2^-7|ref| + 2^-12 rms(ref) of the exact sum.
-    fast=True: one pass with the hardware's 8-token truncating reduction.
+    fast=False: bf16 MFMAs on the exactly converted MX operands (the exact sum up to f32
+    accumulation and the bf16 rounding).
+    fast=True: the block-scaled fp8 MFMA with the hardware's 8-token truncating reduction.
     """
     _dev(a, "a", _U8); _dev(b, "b", _U8)
     _dev(scale_a, "scale_a", _U8); _dev(scale_b, "scale_b", _U8)
@@ -127,6 +128,8 @@ def mx_quantize(x, q=None, s=None, rule="floor"):
     if s is None:
         s = torch.empty((R, max(L // 32, 1)), dtype=torch.uint8, device=x.device)
     _dev(q, "q", _U8); _dev(s, "s", _U8)
+    if q.shape != (R, L) or s.shape != (R, max(L // 32, 1)):
+        raise ValueError("q must be [R, L] and s [R, L/32]")
     call("moe_gg_mx_quantize" + suffix, x.data_ptr(), q.data_ptr(), s.data_ptr(), R, L, _stream())
     return q, s
 
@@ -190,5 +193,7 @@ def row_experts(expert_off, M, out=None):
     if out is None:
         out = torch.empty((M,), dtype=torch.int32, device=expert_off.device)
     _dev(out, "out", (torch.int32,))
+    if out.numel() != M:
+        raise ValueError("out must hold M entries")
     call("moe_gg_row_experts", expert_off.data_ptr(), E, int(M), out.data_ptr(), _stream())
     return out

@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 import workloads as wl
-from gpu_helpers import dev, host, require_gpu, sample_rows, say
+from gpu_helpers import dev, host, require_gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -90,17 +90,19 @@ def test_dgrad_workloads_full(idx):
     assert oracle.dgrad_ok(got, ref, N), (np.max(np.abs(got - ref)), oracle.dgrad_bound(ref, N))
 
 
-def test_dgrad_many_small_sampled():
+def test_dgrad_many_small_full():
+    """The 64-expert workload at full size (the bench's shapes and launch), the whole dx against the
+    oracle's whole dx."""
     torch, mg = require_gpu()
     inp = wl.make_dgrad_inputs(5)
     off = inp["off"]
     M, N = inp["g"].shape
-    say("dgrad workload 5 full size")
+    say("dgrad workload 5 full size, whole output")
     out = mg.dgrad_f32(dev(torch, inp["g"]), dev(torch, inp["W"]), dev(torch, off))
     torch.cuda.synchronize()
-    rng = np.random.default_rng(55)
-    bounds = [int(o) for o in off] + [int(o) - 1 for o in off]
-    rows = sample_rows(rng, M, 160, must=bounds)
-    ref = oracle.dgrad_rows(inp["g"], inp["W"], off, rows)
-    got = host(out[torch.from_numpy(rows).to(out.device)]).astype(np.float64)
-    assert oracle.dgrad_ok(got, ref, N), np.max(np.abs(got - ref))
+    got = host(out).astype(np.float64)
+    del out
+    ref = oracle.dgrad(inp["g"], inp["W"], off)
+    err = float(np.max(np.abs(got - ref)))
+    say(f"dgrad workload 5: max err {err:.4g}, bound {oracle.dgrad_bound(ref, N):.4g}")
+    assert oracle.dgrad_ok(got, ref, N), err
