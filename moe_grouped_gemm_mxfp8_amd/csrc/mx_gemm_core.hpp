@@ -254,7 +254,7 @@ __device__ __forceinline__ void compute_step(const uint8_t *st, v16f (&acc)[4][2
 // v_cvt_scalef32_pk_bf16_fp8 (two codes per instruction, the block's scale
 // 2^(s - 127) as the f32 multiplier) and multiplies them on
 // v_mfma_f32_32x32x16_bf16: 8 chunks of 16 elements, lane l holding row l%32
-// and elements 8(l/32) .. +7 of the chunk (8 bytes of the staged row).  The
+// and 8 elements of the chunk (lane group l/32 the other 8).  The
 // accumulators have the fp8 MFMA's 32 x 32 layout, so the epilogues serve both.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
@@ -273,9 +273,14 @@ __device__ __forceinline__ bf16x8 cvt8(uint32_t w0, uint32_t w1, float scale) {
 }
 
 // One 128-element step of a wave's 128 x 64 patch in the exact form (64
-// bf16 MFMAs).  Contraction elements outside [rlo, rhi) (step-relative) are
-// zeroed in the B-operand codes before the conversion.  Each chunk's
-// fragments are read and converted while the previous chunk's MFMAs run.
+// bf16 MFMAs).  Elements are taken 32 at a time (one scale block j): lane
+// group g reads the 16 bytes of elements 32j + 16g .. +15 of its row with one
+// 16-byte LDS read (8-byte reads measured at half the LDS throughput) and
+// feeds bytes 0-7 to chunk 2j and bytes 8-15 to chunk 2j + 1, the same
+// mapping for both operands, so every chunk's products pair the same tokens.
+// Contraction elements outside [rlo, rhi) (step-relative) are zeroed in the
+// B-operand codes before the conversion.  The next block's bytes are read
+// while the current block's MFMAs run.
 __device__ __forceinline__ void compute_step_bf16(const uint8_t *st, v16f (&acc)[4][2], const uint32_t (&xrow)[4],
                                                   const uint32_t (&grow)[2], int wk, int wn, int l32, int g,
                                                   int rlo, int rhi) {
@@ -285,40 +290,50 @@ __device__ __forceinline__ void compute_step_bf16(const uint8_t *st, v16f (&acc)
 #pragma unroll
   for (int b = 0; b < 2; ++b) sg[b] = *reinterpret_cast<const uint32_t *>(st + ST_SB + 4 * (wn * 64 + b * 32 + l32));
   const bool masked = rlo > 0 || rhi < TT;
-  auto load = [&](int c, bf16x8 (&xa)[4], bf16x8 (&gb)[2]) {
-    const int blk = c >> 1;                        // 32-element scale block of chunk c
+  auto read = [&](int j, v4u (&xr)[4], v4u (&gr)[2]) {
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const v2u w = *reinterpret_cast<const v2u *>(st + xrow[a] + 16 * c + 8 * g);
-      xa[a] = cvt8(w[0], w[1], e8m0_f32(sx[a], blk));
-    }
+    for (int a = 0; a < 4; ++a) xr[a] = *reinterpret_cast<const v4u *>(st + xrow[a] + 32 * j + 16 * g);
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      v2u w = *reinterpret_cast<const v2u *>(st + grow[b] + 16 * c + 8 * g);
+      gr[b] = *reinterpret_cast<const v4u *>(st + grow[b] + 32 * j + 16 * g);
       if (masked) {
-        const int t = 16 * c + 8 * g;               // step-relative element of byte 0
-        w[0] &= keep_bytes(rlo - t, rhi - t);
-        w[1] &= keep_bytes(rlo - t - 4, rhi - t - 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = 32 * j + 16 * g + 4 * i;    // step-relative element of byte 0 of dword i
+          gr[b][i] &= keep_bytes(rlo - t, rhi - t);
+        }
       }
-      gb[b] = cvt8(w[0], w[1], e8m0_f32(sg[b], blk));
     }
   };
-  bf16x8 xa[4], gb[2];
-  load(0, xa, gb);
+  v4u xr[4], gr[2];
+  read(0, xr, gr);
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    bf16x8 xn[4], gn[2];
-    if (c < 7) load(c + 1, xn, gn);
+  for (int j = 0; j < 4; ++j) {
+    v4u xn[4], gn[2];
+    if (j < 3) read(j + 1, xn, gn);
+    float fx[4], fg[2];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < 4; ++a) fx[a] = e8m0_f32(sx[a], j);
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
-        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[a], gb[b], acc[a][b], 0, 0, 0);
-    if (c < 7) {
+    for (int b = 0; b < 2; ++b) fg[b] = e8m0_f32(sg[b], j);
 #pragma unroll
-      for (int a = 0; a < 4; ++a) xa[a] = xn[a];
+    for (int q = 0; q < 2; ++q) {
+      bf16x8 xa[4], gb[2];
 #pragma unroll
-      for (int b = 0; b < 2; ++b) gb[b] = gn[b];
+      for (int a = 0; a < 4; ++a) xa[a] = cvt8(xr[a][2 * q], xr[a][2 * q + 1], fx[a]);
+#pragma unroll
+      for (int b = 0; b < 2; ++b) gb[b] = cvt8(gr[b][2 * q], gr[b][2 * q + 1], fg[b]);
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[a], gb[b], acc[a][b], 0, 0, 0);
+    }
+    if (j < 3) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) xr[a] = xn[a];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) gr[b] = gn[b];
     }
   }
 }
