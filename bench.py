@@ -255,12 +255,14 @@ def bench_grouped(torch, mg, idx, steps, warmup, cpu_baseline, fast=False):
         (N * K + N * K // 32) for e in range(E) if inp["off"][e + 1] > inp["off"][e])
     line = {"metric": f"TFLOP/s, expert-grouped MXFP8 GEMM as the data gradient of workload {idx} (1 GPU)",
             "value": round(tf, 2), "unit": "TFLOP/s", "pct_of_fp8_peak": round(100 * tf / PEAK_FP8_TFLOPS, 2),
-            "ms_per_step": round(ms, 4), "dtype": "fp8e4m3*fp8e4m3->f32 acc, bf16 out",
-            "mode": "single block-scaled MFMA pass" if fast else "two block-scaled MFMA passes (A codes >= 128 / the rest)",
+            "ms_per_step": round(ms, 4), "dtype": "fp8e4m3*fp8e4m3->f32 acc, bf16 out" if fast else "mxfp8 (e4m3+e8m0) -> bf16 MFMA, f32 acc, bf16 out",
+            "mode": "single block-scaled fp8 MFMA pass" if fast else "exact: MX operands converted to bf16, bf16 MFMA",
             "config": {"workload": wl.WORKLOADS[idx].name, "E": E, "M": M, "contraction": N, "N_out": K},
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf / PEAK_FP8_TFLOPS, 4),
                          "traffic": None if fast else read_traffic("grouped", idx),
+                         "mfma": "v_mfma_scale_f32_32x32x64_f8f6f4 (fp8)" if fast else "v_mfma_f32_32x32x16_bf16",
+                         "frac_of_mfma_dtype_peak": round(tf / (PEAK_FP8_TFLOPS if fast else PEAK_BF16_TFLOPS), 4),
                          "algorithmic_bytes": int(nbytes), "algorithmic_flop": flop}}
     bind_roofline(line, flop, nbytes, ms)
     if cpu_baseline:
@@ -310,12 +312,15 @@ def bench_forward(torch, mg, idx, steps, warmup, cpu_baseline, fast=False, fp4=F
     line = {"metric": f"TFLOP/s, MoE forward y = x W_e^T ({'MXFP4' if fp4 else 'MXFP8'} weights) on workload {idx} (1 GPU)",
             "value": round(tf, 2), "unit": "TFLOP/s", "pct_of_fp8_peak": round(100 * tf / PEAK_FP8_TFLOPS, 2),
             "ms_per_step": round(ms, 4),
-            "dtype": ("fp8e4m3*fp4e2m1" if fp4 else "fp8e4m3*fp8e4m3") + "->f32 acc, bf16 out",
-            "mode": "single block-scaled MFMA pass" if fast else "two block-scaled MFMA passes (A codes >= 128 / the rest)",
+            "dtype": (("fp8e4m3*fp4e2m1" if fp4 else "fp8e4m3*fp8e4m3") + "->f32 acc, bf16 out") if fast
+                     else ("mxfp8 x mxfp4" if fp4 else "mxfp8 x mxfp8") + " -> bf16 MFMA, f32 acc, bf16 out",
+            "mode": "single block-scaled fp8 MFMA pass" if fast else "exact: MX operands converted to bf16, bf16 MFMA",
             "config": {"workload": wl.WORKLOADS[idx].name, "E": E, "M": M, "K_in": K, "N_out": N},
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf / PEAK_FP8_TFLOPS, 4),
                          "traffic": None if fast else read_traffic(name, idx),
+                         "mfma": "v_mfma_scale_f32_32x32x64_f8f6f4 (fp8)" if fast else "v_mfma_f32_32x32x16_bf16",
+                         "frac_of_mfma_dtype_peak": round(tf / (PEAK_FP8_TFLOPS if fast else PEAK_BF16_TFLOPS), 4),
                          "algorithmic_bytes": int(nbytes), "algorithmic_flop": flop}}
     bind_roofline(line, flop, nbytes, ms)
     if cpu_baseline:

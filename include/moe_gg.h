@@ -171,16 +171,11 @@ MOE_GG_API int moe_gg_dgrad_f32(const float *A, const float *B, float *C,
  *
  * Shapes: M, N, K >= 0, E >= 1 and K % 32 == 0 (EINVAL otherwise; K = 0
  * writes +0.0 everywhere); N % 256 == 0,
- * K % 128 == 0 and E <= 2048 (EUNSUPPORTED otherwise).  Accuracy: the
- * block-scaled fp8 MFMA truncates each 8-element run's products (see the
- * weight gradient), so this entry point splits A's codes into two MFMA
- * passes: in each 128-element step, a code whose value stands out against the
- * quietest of its row's four 32-element blocks (exponent field >= 16 +
- * s_min - s_j, s_j its block's scale byte) goes to the first pass, the rest
- * to the second.  With outliers in A only (64x outliers in activations or
- * gradients, weights without outliers of their own) this keeps the result
- * within 2^-7 |ref| + 2^-12 rms(ref) of the exact sum; outliers in both
- * operands can exceed it where they meet.
+ * K % 128 == 0 and E <= 2048 (EUNSUPPORTED otherwise).  Accuracy as for the
+ * weight gradient: the codes, times their scales, are converted exactly to
+ * bf16 and multiplied on the bf16 MFMA with f32 accumulation, so the result
+ * is the exact sum up to f32 accumulation and the bf16 rounding on any input
+ * (outliers in either operand or both).
  */
 MOE_GG_API int moe_gg_grouped_mxfp8(const uint8_t *A, const uint8_t *B, uint16_t *C,
                                     const uint8_t *scale_A, const uint8_t *scale_B,
@@ -216,9 +211,9 @@ MOE_GG_API int moe_gg_grouped_mxfp8_fast(const uint8_t *A, const uint8_t *B, uin
  *   C[m][j] = bf16_rne( sum over c of deq(A)[m][c] deq4(B[e(m)])[j][c] )
  *
  * The MoE forward y = x W_e^T with A = MX(x) along K and B[e] = MXFP4(W_e)
- * along K.  Shapes and status codes as moe_gg_grouped_mxfp8; the default
- * entry point splits A's codes into two MFMA passes as moe_gg_grouped_mxfp8
- * does, the _fast one makes one.
+ * along K.  Shapes, status codes and accuracy as moe_gg_grouped_mxfp8 (an
+ * E2M1 value times its E8M0 scale is exactly a bf16 too); the _fast entry
+ * point makes one block-scaled MFMA pass with format 4 for B.
  */
 MOE_GG_API int moe_gg_grouped_a8w4(const uint8_t *A, const uint8_t *B, uint16_t *C,
                                    const uint8_t *scale_A, const uint8_t *scale_B,

@@ -1,7 +1,7 @@
 // Expert-grouped MXFP8 GEMM on gfx950:
 //   C[m][j] = sum over c of A[m][c] * B[e(m)][j][c]
 // with E4M3 elements and one E8M0 scale per 32 contraction elements on both
-// operands, f32 accumulation in the block-scaled MFMA, bf16 output.  Token
+// operands, f32 accumulation, bf16 output.  Token
 // rows m are bucketed by expert through the offsets (the tinygrad page's
 // expert_off; e(m) is the Slang page's expert_for_row), and each expert has
 // its own MXFP8 weight matrix B[e] with scales along the contraction (the
@@ -23,8 +23,14 @@
 //  * Roles in the core: the weight tile B[e][j0..j0+255][c..c+127] is the
 //    x-role (MFMA A operand; output rows j), the token tile A[m0..][c..] the
 //    g-role (MFMA B operand; output columns m), so the epilogue writes
-//    C[m][j] as whole 128-byte row pieces.  The two-pass form splits the
-//    token operand's codes (activations and gradients carry the outliers).
+//    C[m][j] as whole 128-byte row pieces.
+//  * Exact form (default entry points): each 32-element block of both tiles
+//    is converted with its scale to bf16 in registers and multiplied on the
+//    bf16 MFMA, the weight gradient's exact step (no token masking: the
+//    contraction here is the feature axis).  The block-scaled fp8 MFMA
+//    truncates each 8-element run's products, which loses small products
+//    where an outlier of one operand meets an outlier of the other; the fast
+//    entry points make that one pass.
 //  * Each 128-element contraction step stages both tiles (32 KB each) and
 //    their scale dwords in LDS with buffer loads that write LDS directly,
 //    double-buffered; the workgroup walks the steps of all its tiles as one
@@ -73,7 +79,9 @@ struct Tile {
   int kind, e, jt, m0, rows;
 };
 
-template <bool SPLIT, bool XFP4>
+// EXACT: operands converted exactly to bf16 and multiplied on the bf16 MFMA;
+// otherwise one block-scaled fp8 MFMA pass.
+template <bool EXACT, bool XFP4>
 __global__ __launch_bounds__(NTHREAD, 1) void grouped_mxfp8_kernel(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, uint16_t *__restrict__ C,
     const uint8_t *__restrict__ SA, const uint8_t *__restrict__ SB,
@@ -305,7 +313,10 @@ __global__ __launch_bounds__(NTHREAD, 1) void grouped_mxfp8_kernel(
         advance();
       }
       const uint8_t *st = smem + buf * STAGE_BYTES;
-      compute_step<SPLIT, XFP4>(st, acc, xrow, grow, chunk_off, wk, wn, l32, g, 0, TT, 0, TB);
+      if constexpr (EXACT)
+        compute_step_bf16<XFP4>(st, acc, xrow, grow, wk, wn, l32, g, 0, TT);
+      else
+        compute_step<XFP4>(st, acc, xrow, grow, chunk_off, wk, wn, l32, g, 0, TT);
       buf ^= 1;
     }
     // ---- epilogue: C[m0 + m][j0 + j] for the tile's rows; the descriptor
@@ -316,7 +327,7 @@ __global__ __launch_bounds__(NTHREAD, 1) void grouped_mxfp8_kernel(
   wait_vmcnt<0>();
 }
 
-int launch_grouped(bool split, bool xfp4, const uint8_t *A, const uint8_t *B, uint16_t *C, const uint8_t *scale_A,
+int launch_grouped(bool exact, bool xfp4, const uint8_t *A, const uint8_t *B, uint16_t *C, const uint8_t *scale_A,
                    const uint8_t *scale_B, const int32_t *expert_off, int M, int N, int K, int E,
                    hipStream_t stream) {
   if (M < 0 || N < 0 || K < 0 || E <= 0 || !expert_off) return MOE_GG_EINVAL;
@@ -342,8 +353,8 @@ int launch_grouped(bool split, bool xfp4, const uint8_t *A, const uint8_t *B, ui
 #define MOE_GG_LAUNCH(S, X)                                                                              \
   hipLaunchKernelGGL((grouped_mxfp8_kernel<S, X>), dim3(grid), dim3(NTHREAD), 0, stream, A, B, C, scale_A, \
                      scale_B, expert_off, M, N, K, E)
-  if (split && xfp4) MOE_GG_LAUNCH(true, true);
-  else if (split) MOE_GG_LAUNCH(true, false);
+  if (exact && xfp4) MOE_GG_LAUNCH(true, true);
+  else if (exact) MOE_GG_LAUNCH(true, false);
   else if (xfp4) MOE_GG_LAUNCH(false, true);
   else MOE_GG_LAUNCH(false, false);
 #undef MOE_GG_LAUNCH

@@ -1,6 +1,7 @@
 // Shared core of the block-scaled MXFP8 GEMM kernels on gfx950: the LDS
 // stage layout, the step of 128 contraction elements for one wave's
-// 128 x 64 patch, the two-pass split of the B-operand codes and the epilogues.
+// 128 x 64 patch (block-scaled fp8 MFMA, or exact on the bf16 MFMA) and the
+// epilogues.
 //
 // A stage holds two operand tiles of 256 rows x 128 contraction bytes (E4M3)
 // and their scale dwords: the A-operand tile (whose rows become the MFMA output
@@ -51,43 +52,6 @@ __device__ __forceinline__ uint32_t tile_row4(int r) {
   return static_cast<uint32_t>(((r >> 6) * 4 + (r & 3)) * BLK4 + ((r & 63) >> 2) * TT4);
 }
 
-// The two-pass split.  The scaled MFMA truncates the products of each run of 8
-// contraction elements to 2^(largest exponent sum of the run - 13), so a run that
-// holds one very large product (an outlier of one operand meeting an outlier of
-// the other) loses most of its other products.  The two-pass form therefore
-// multiplies the B-operand codes whose VALUE stands out in two groups: pass one
-// takes the codes at least about 2^9 times the 32-block quantisation step of the
-// row's quietest block in the 128-element step, pass two the rest.  With E8M0
-// scale bytes s_j of the step's four blocks and s_min = min s_j, a code of block j
-// goes to pass one iff its exponent field is >= t_j = clamp(16 + s_min - s_j, 0, 16):
-// in the quietest block never (fields go to 15), in a block whose scale is 2^d
-// larger every code whose value exceeds ~2^(9 - d + ...) of that block's max,
-// which catches every outlier code of an outlier block (also a second, smaller
-// one that the block's scale leaves far below the top binade) while the ordinary
-// values stay in pass two.  Comparing fields, not values, keeps it exact and cheap.
-//
-// split_const(t) replicates 0x80 - 8t into each byte; for a dword v of codes,
-// y = (v & 0x78787878) + split_const(t) has bit 7 set in exactly the bytes whose
-// exponent field (bits 3-6) is >= t, with no carry between bytes (at most
-// 0x78 + 0x80).  v_perm_b32 selectors 8-11 broadcast the top bit of bytes 1 and 3
-// of each source, so y supplies bytes 1 and 3 and y << 8 bytes 0 and 2 of the mask.
-__device__ __forceinline__ uint32_t split_const(int t) {
-  return 0x80808080u - static_cast<uint32_t>(t) * 0x08080808u;
-}
-__device__ __forceinline__ uint32_t pass_one_mask(uint32_t v, uint32_t c) {
-  const uint32_t y = (v & 0x78787878u) + c;
-  return __builtin_amdgcn_perm(y << 8, y, 0x090B080Au);
-}
-// The four per-block constants of one row from its step's scale dword (block j in byte j).
-__device__ __forceinline__ void split_consts(uint32_t sdw, uint32_t (&c)[4]) {
-  int sj[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) sj[j] = static_cast<int>((sdw >> (8 * j)) & 0xFFu);
-  const int smin = min(min(sj[0], sj[1]), min(sj[2], sj[3]));
-#pragma unroll
-  for (int j = 0; j < 4; ++j) c[j] = split_const(max(16 + smin - sj[j], 0));
-}
-
 // Zeroes the codes of the contraction elements outside [rlo, rhi)
 // (step-relative) in a B-operand fragment of 64-element half h: dword i of lane group g holds tokens
 // 64h + 16g + 4i .. +3 (i < 4) and 64h + 32 + 16g + 4(i-4) .. +3 (i >= 4).  A
@@ -110,28 +74,24 @@ __device__ __forceinline__ void mask_tokens(v8i &frag, int h, int g, int rlo, in
 }
 
 // One 128-step of the contraction for a wave's 128 x 64 patch: 16
-// block-scaled MFMAs (32 in the two-pass form).  The A-operand tile (rows =
+// block-scaled MFMAs.  The A-operand tile (rows =
 // output rows of the MFMA) and the B-operand tile (rows = output columns) sit
-// at ST_A and ST_B of stage st.  Contraction elements outside [rlo, rhi) and
-// B-operand rows outside [row_lo, row_hi) are zeroed in the B-operand
-// fragments first (both bounds step- and tile-relative).  The fragments of
+// at ST_A and ST_B of stage st.  Contraction elements outside [rlo, rhi)
+// (step-relative) are zeroed in the B-operand fragments first.  The fragments of
 // both 64-element halves are read from LDS up front and the MFMAs of the
 // first half are interleaved with the reads of the second, so only the first
 // reads' latency is exposed.
-template <bool SPLIT, bool XFP4 = false>
+template <bool XFP4 = false>
 __device__ __forceinline__ void compute_step(const uint8_t *st, v16f (&acc)[4][2], const uint32_t (&xrow)[4],
                                              const uint32_t (&grow)[2], const uint32_t (&chunk_off)[2][2],
-                                             int wk, int wn, int l32, int g, int rlo, int rhi, int row_lo,
-                                             int row_hi) {
-  uint32_t sx[4], sg[2], sgraw[2];
+                                             int wk, int wn, int l32, int g, int rlo, int rhi) {
+  uint32_t sx[4], sg[2];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
     sx[a] = *reinterpret_cast<const uint32_t *>(st + ST_SA + 4 * (wk * 128 + a * 32 + l32)) >> (8 * g);
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    sgraw[b] = *reinterpret_cast<const uint32_t *>(st + ST_SB + 4 * (wn * 64 + b * 32 + l32));
-    sg[b] = sgraw[b] >> (8 * g);
-  }
+  for (int b = 0; b < 2; ++b)
+    sg[b] = *reinterpret_cast<const uint32_t *>(st + ST_SB + 4 * (wn * 64 + b * 32 + l32)) >> (8 * g);
   auto frag = [&](uint32_t row, int h) {
     const v4i lo = *reinterpret_cast<const v4i *>(st + row + chunk_off[h][0]);
     const v4i hi = *reinterpret_cast<const v4i *>(st + row + chunk_off[h][1]);
@@ -172,74 +132,26 @@ __device__ __forceinline__ void compute_step(const uint8_t *st, v16f (&acc)[4][2
       mask_tokens(g1[b], 1, g, rlo, rhi);
     }
   }
-  if (row_lo > 0 || row_hi < TB) {
-    // B-operand rows outside [row_lo, row_hi) take no part (rows of another expert)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int row = wn * 64 + b * 32 + l32;
-      const bool in = row >= row_lo && row < row_hi;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        g0[b][i] = in ? g0[b][i] : 0;
-        g1[b][i] = in ? g1[b][i] : 0;
-      }
-    }
+  for (int a = 0; a < 4; ++a) {
+    mm(a, 0, x[a], g0[0], 0);
+    mm(a, 1, x[a], g0[1], 0);
+    x[a] = xfrag(xrow[a], 1);
   }
-  if constexpr (SPLIT) {
-    // two passes over the B-operand codes (pass_one_mask above), so that no
-    // 8-element run of the MFMA mixes a standing-out value with ordinary ones.
-    // Dwords 0-3 of a lane's half-h fragment hold block 2h of the step, dwords
-    // 4-7 block 2h + 1.  The passes over one accumulator are 8 MFMAs apart (no
-    // result-latency stall).
-    uint32_t sc[2][4];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) split_consts(sgraw[b], sc[b]);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      v8i gh[2], gl[2];
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t v = static_cast<uint32_t>(h == 0 ? g0[b][i] : g1[b][i]);
-          const uint32_t m = pass_one_mask(v, sc[b][2 * h + (i >> 2)]);
-          gh[b][i] = static_cast<int>(v & m);
-          gl[b][i] = static_cast<int>(v ^ (v & m));
-        }
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        mm(a, 0, x[a], gh[0], h);
-        mm(a, 1, x[a], gh[1], h);
-      }
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        mm(a, 0, x[a], gl[0], h);
-        mm(a, 1, x[a], gl[1], h);
-        if (h == 0) x[a] = xfrag(xrow[a], 1);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      mm(a, 0, x[a], g0[0], 0);
-      mm(a, 1, x[a], g0[1], 0);
-      x[a] = xfrag(xrow[a], 1);
-    }
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      mm(a, 0, x[a], g1[0], 1);
-      mm(a, 1, x[a], g1[1], 1);
-    }
-    // scales and first-half reads, then MFMAs with the second half's x reads between
-    // (an fp4 x fragment is one 16-byte read instead of two)
-    __builtin_amdgcn_sched_group_barrier(0x100, XFP4 ? 18 : 22, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, XFP4 ? 1 : 2, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+  for (int a = 0; a < 4; ++a) {
+    mm(a, 0, x[a], g1[0], 1);
+    mm(a, 1, x[a], g1[1], 1);
   }
+  // scales and first-half reads, then MFMAs with the second half's x reads between
+  // (an fp4 x fragment is one 16-byte read instead of two)
+  __builtin_amdgcn_sched_group_barrier(0x100, XFP4 ? 18 : 22, 0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, XFP4 ? 1 : 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
 }
 
 // The exact form of a 128-element step.  The scaled fp8 MFMA truncates the
@@ -271,6 +183,15 @@ __device__ __forceinline__ bf16x8 cvt8(uint32_t w0, uint32_t w1, float scale) {
   const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, scale, true);
   return (bf16x8){p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
+// The same for eight E2M1 codes (one dword, element 2i in the low nibble of
+// byte i): an E2M1 value times its E8M0 scale is exactly a bf16 as well.
+__device__ __forceinline__ bf16x8 cvt8_fp4(uint32_t w, float scale) {
+  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
+  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
+  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
+  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
+  return (bf16x8){p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
 
 // One 128-element step of a wave's 128 x 64 patch in the exact form (64
 // bf16 MFMAs).  Elements are taken 32 at a time (one scale block j): lane
@@ -280,7 +201,10 @@ __device__ __forceinline__ bf16x8 cvt8(uint32_t w0, uint32_t w1, float scale) {
 // mapping for both operands, so every chunk's products pair the same tokens.
 // Contraction elements outside [rlo, rhi) (step-relative) are zeroed in the
 // B-operand codes before the conversion.  The next block's bytes are read
-// while the current block's MFMAs run.
+// while the current block's MFMAs run.  An fp4 A-operand tile (XFP4) holds the
+// same 16 elements of a lane in 8 bytes (dword 0 for chunk 2j, dword 1 for
+// chunk 2j + 1).
+template <bool XFP4 = false>
 __device__ __forceinline__ void compute_step_bf16(const uint8_t *st, v16f (&acc)[4][2], const uint32_t (&xrow)[4],
                                                   const uint32_t (&grow)[2], int wk, int wn, int l32, int g,
                                                   int rlo, int rhi) {
@@ -292,7 +216,14 @@ __device__ __forceinline__ void compute_step_bf16(const uint8_t *st, v16f (&acc)
   const bool masked = rlo > 0 || rhi < TT;
   auto read = [&](int j, v4u (&xr)[4], v4u (&gr)[2]) {
 #pragma unroll
-    for (int a = 0; a < 4; ++a) xr[a] = *reinterpret_cast<const v4u *>(st + xrow[a] + 32 * j + 16 * g);
+    for (int a = 0; a < 4; ++a) {
+      if constexpr (XFP4) {
+        const v2u w = *reinterpret_cast<const v2u *>(st + xrow[a] + 16 * j + 8 * g);
+        xr[a] = (v4u){w[0], w[1], 0u, 0u};
+      } else {
+        xr[a] = *reinterpret_cast<const v4u *>(st + xrow[a] + 32 * j + 16 * g);
+      }
+    }
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       gr[b] = *reinterpret_cast<const v4u *>(st + grow[b] + 32 * j + 16 * g);
@@ -320,7 +251,8 @@ __device__ __forceinline__ void compute_step_bf16(const uint8_t *st, v16f (&acc)
     for (int q = 0; q < 2; ++q) {
       bf16x8 xa[4], gb[2];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) xa[a] = cvt8(xr[a][2 * q], xr[a][2 * q + 1], fx[a]);
+      for (int a = 0; a < 4; ++a)
+        xa[a] = XFP4 ? cvt8_fp4(xr[a][q], fx[a]) : cvt8(xr[a][2 * q], xr[a][2 * q + 1], fx[a]);
 #pragma unroll
       for (int b = 0; b < 2; ++b) gb[b] = cvt8(gr[b][2 * q], gr[b][2 * q + 1], fg[b]);
 #pragma unroll

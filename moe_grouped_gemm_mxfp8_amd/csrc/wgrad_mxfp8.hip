@@ -277,7 +277,7 @@ __global__ __launch_bounds__(NTHREAD, 1) void wgrad_mxfp8_kernel(
       if constexpr (EXACT)
         compute_step_bf16(st, acc, xrow, grow, wk, wn, l32, g, cur.lo - s * TT, cur.hi - s * TT);
       else
-        compute_step<false>(st, acc, xrow, grow, chunk_off, wk, wn, l32, g, cur.lo - s * TT, cur.hi - s * TT, 0, TB);
+        compute_step(st, acc, xrow, grow, chunk_off, wk, wn, l32, g, cur.lo - s * TT, cur.hi - s * TT);
       buf ^= 1;
     }
 

@@ -101,6 +101,44 @@ def test_a8w4_small(name):
     assert oracle.wgrad_excess(got, ref) <= 0, oracle.wgrad_excess(got, ref)
 
 
+@pytest.mark.parametrize("name", ["straddle", "ragged_m", "deep_k"])
+def test_a8w4_outliers_in_both_operands(name):
+    """1% x64 outliers in the tokens and in the fp4 weights."""
+    torch, mg = require_gpu()
+    N, K, counts = CASES[name]
+    off = wl.offsets_from_counts(counts)
+    M, E = int(off[-1]), len(counts)
+    rng = np.random.default_rng(len(name) * 23 + K)
+    a = rng.standard_normal((M, K)).astype(np.float32)
+    a[rng.random(a.shape) < 0.01] *= 64
+    w = rng.standard_normal((E, N, K)).astype(np.float32)
+    w[rng.random(w.shape) < 0.01] *= 64
+    ca, sa = oracle.mx_quantize(a)
+    cb, sb = _quant_b4(w)
+    say("a8w4, outliers in both operands", name, M, N, K, counts)
+    got = _run(torch, mg, ca, sa, cb, sb, off)
+    ref = oracle.grouped_gemm(ca, sa, cb, sb, off, b_format="e2m1")
+    assert oracle.wgrad_excess(got, ref) <= 0, oracle.wgrad_excess(got, ref)
+
+
+def test_a8w4_nibble_order():
+    """Weights with 1.0 in the low nibble and 0 in the high one (byte 0x02) against token
+    codes that differ between even and odd elements: only the even elements may count."""
+    torch, mg = require_gpu()
+    counts = [256]
+    off = wl.offsets_from_counts(counts)
+    M, N, K, E = 256, 256, 256, 1
+    ca = np.tile(np.array([0x38, 0x40], np.uint8), (M, K // 2))    # 1.0 at even, 2.0 at odd elements
+    sa = np.full((M, K // 32), 127, np.uint8)
+    cb = np.full((E, N, K // 2), 0x02, np.uint8)
+    sb = np.full((E, N, K // 32), 127, np.uint8)
+    say("a8w4 nibble order")
+    got = _run(torch, mg, ca, sa, cb, sb, off)
+    assert np.all(got == float(K // 2))
+    got_fast = _run(torch, mg, ca, sa, cb, sb, off, fast=True)
+    assert np.all(got_fast == float(K // 2))
+
+
 def test_a8w4_all_ones_and_expert_scales_exact():
     """A codes 1.0, B codes 1.0 with expert e's scales 2^e: row m gets K * 2^e(m), exactly."""
     torch, mg = require_gpu()

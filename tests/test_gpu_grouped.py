@@ -59,6 +59,28 @@ def test_grouped_small(name):
     assert oracle.wgrad_excess(got, ref) <= 0, oracle.wgrad_excess(got, ref)
 
 
+@pytest.mark.parametrize("name", ["aligned", "straddle", "ragged_m", "many_per_tile"])
+def test_grouped_outliers_in_both_operands(name):
+    """1% x64 outliers in the tokens and in the weights: where two outliers meet, the
+    block-scaled fp8 MFMA's truncation of an 8-element run would lose the run's other
+    products; the default entry point multiplies exactly converted bf16 operands."""
+    torch, mg = require_gpu()
+    N, K, counts = CASES[name]
+    off = wl.offsets_from_counts(counts)
+    M, E = int(off[-1]), len(counts)
+    rng = np.random.default_rng(len(name) * 19 + K)
+    a = rng.standard_normal((M, K)).astype(np.float32)
+    a[rng.random(a.shape) < 0.01] *= 64
+    w = rng.standard_normal((E, N, K)).astype(np.float32)
+    w[rng.random(w.shape) < 0.01] *= 64
+    ca, sa = oracle.mx_quantize(a)
+    cb, sb = _quant_b(w)
+    say("grouped, outliers in both operands", name, M, N, K, counts)
+    got = _run(torch, mg, ca, sa, cb, sb, off)
+    ref = oracle.grouped_gemm(ca, sa, cb, sb, off)
+    assert oracle.wgrad_excess(got, ref) <= 0, oracle.wgrad_excess(got, ref)
+
+
 def test_grouped_all_ones_is_exact():
     torch, mg = require_gpu()
     counts = [100, 0, 400, 12]
