@@ -314,7 +314,7 @@ __global__ __launch_bounds__(NTHREAD, 1) void grouped_mxfp8_kernel(
       }
       const uint8_t *st = smem + buf * STAGE_BYTES;
       if constexpr (EXACT)
-        compute_step_bf16<XFP4>(st, acc, xrow, grow, wk, wn, l32, g, 0, TT);
+        compute_step_bf16<XFP4>(st, acc, xrow, grow, wk, wn, l32, g);
       else
         compute_step<XFP4>(st, acc, xrow, grow, chunk_off, wk, wn, l32, g, 0, TT);
       buf ^= 1;

@@ -193,27 +193,50 @@ __device__ __forceinline__ bf16x8 cvt8_fp4(uint32_t w, float scale) {
   return (bf16x8){p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
+// Zeroes the codes of the step's contraction elements outside [rlo, rhi)
+// (step-relative) in the B-operand tile of a stage, in LDS: thread t of the
+// 512 rewrites bytes 64(t%2) .. +63 of row t/2.  A zero code makes the product
+// zero, so the step then sums the expert's tokens only (the weight gradient's
+// first and last step of an expert whose bounds are not multiples of 128).
+// The caller separates it from the stage's readers by barriers.
+__device__ __forceinline__ void mask_stage_elements(uint8_t *st, int tid, int rlo, int rhi) {
+  const int row = tid >> 1, h = tid & 1;
+  uint8_t *p = st + ST_B + tile_row(row) + 64 * h;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    v4u v = *reinterpret_cast<const v4u *>(p + 16 * c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 64 * h + 16 * c + 4 * i;      // step-relative element of byte 0 of dword i
+      v[i] &= keep_bytes(rlo - t, rhi - t);
+    }
+    *reinterpret_cast<v4u *>(p + 16 * c) = v;
+  }
+}
+
 // One 128-element step of a wave's 128 x 64 patch in the exact form (64
 // bf16 MFMAs).  Elements are taken 32 at a time (one scale block j): lane
 // group g reads the 16 bytes of elements 32j + 16g .. +15 of its row with one
 // 16-byte LDS read (8-byte reads measured at half the LDS throughput) and
 // feeds bytes 0-7 to chunk 2j and bytes 8-15 to chunk 2j + 1, the same
 // mapping for both operands, so every chunk's products pair the same tokens.
-// Contraction elements outside [rlo, rhi) (step-relative) are zeroed in the
-// B-operand codes before the conversion.  The next block's bytes are read
-// while the current block's MFMAs run.  An fp4 A-operand tile (XFP4) holds the
+// The step masks no element (mask_stage_elements zeroes them in the stage
+// beforehand): a run-time mask test inside the block loop split it into basic
+// blocks, at whose edges every read of the next block waited for its data
+// before the current block's MFMAs (measured in the generated code).  The
+// next block's bytes are read while the current block's MFMAs run; a
+// scheduling fence per block keeps later blocks' reads from being hoisted
+// (their registers would spill).  An fp4 A-operand tile (XFP4) holds the
 // same 16 elements of a lane in 8 bytes (dword 0 for chunk 2j, dword 1 for
 // chunk 2j + 1).
 template <bool XFP4 = false>
 __device__ __forceinline__ void compute_step_bf16(const uint8_t *st, v16f (&acc)[4][2], const uint32_t (&xrow)[4],
-                                                  const uint32_t (&grow)[2], int wk, int wn, int l32, int g,
-                                                  int rlo, int rhi) {
+                                                  const uint32_t (&grow)[2], int wk, int wn, int l32, int g) {
   uint32_t sx[4], sg[2];
 #pragma unroll
   for (int a = 0; a < 4; ++a) sx[a] = *reinterpret_cast<const uint32_t *>(st + ST_SA + 4 * (wk * 128 + a * 32 + l32));
 #pragma unroll
   for (int b = 0; b < 2; ++b) sg[b] = *reinterpret_cast<const uint32_t *>(st + ST_SB + 4 * (wn * 64 + b * 32 + l32));
-  const bool masked = rlo > 0 || rhi < TT;
   auto read = [&](int j, v4u (&xr)[4], v4u (&gr)[2]) {
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
@@ -225,16 +248,7 @@ __device__ __forceinline__ void compute_step_bf16(const uint8_t *st, v16f (&acc)
       }
     }
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      gr[b] = *reinterpret_cast<const v4u *>(st + grow[b] + 32 * j + 16 * g);
-      if (masked) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = 32 * j + 16 * g + 4 * i;    // step-relative element of byte 0 of dword i
-          gr[b][i] &= keep_bytes(rlo - t, rhi - t);
-        }
-      }
-    }
+    for (int b = 0; b < 2; ++b) gr[b] = *reinterpret_cast<const v4u *>(st + grow[b] + 32 * j + 16 * g);
   };
   v4u xr[4], gr[2];
   read(0, xr, gr);
@@ -267,6 +281,8 @@ __device__ __forceinline__ void compute_step_bf16(const uint8_t *st, v16f (&acc)
 #pragma unroll
       for (int b = 0; b < 2; ++b) gr[b] = gn[b];
     }
+    // keep the scheduler from hoisting later blocks' reads (register pressure)
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 

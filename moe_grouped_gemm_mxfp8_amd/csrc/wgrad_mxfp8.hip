@@ -273,10 +273,15 @@ __global__ __launch_bounds__(NTHREAD, 1) void wgrad_mxfp8_kernel(
         advance(ld);
       }
 
-      const uint8_t *st = smem + buf * STAGE_BYTES;
-      if constexpr (EXACT)
-        compute_step_bf16(st, acc, xrow, grow, wk, wn, l32, g, cur.lo - s * TT, cur.hi - s * TT);
-      else
+      uint8_t *st = smem + buf * STAGE_BYTES;
+      if constexpr (EXACT) {
+        const int rlo = cur.lo - s * TT, rhi = cur.hi - s * TT;
+        if (rlo > 0 || rhi < TT) {             // an expert's partial first or last step
+          mask_stage_elements(st, tid, rlo, rhi);
+          barrier();
+        }
+        compute_step_bf16(st, acc, xrow, grow, wk, wn, l32, g);
+      } else
         compute_step(st, acc, xrow, grow, chunk_off, wk, wn, l32, g, cur.lo - s * TT, cur.hi - s * TT);
       buf ^= 1;
     }
