@@ -329,12 +329,19 @@ __device__ __forceinline__ void store_tile(const v16f (&acc)[4][2], uint8_t *stg
         }
       }
     asm volatile("" ::: "memory");
+    // all eight row pieces first, then the stores: one LDS round trip per
+    // chunk instead of one per store
+    v4u v[8];
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
       const int row = p * 8 + (lane >> 3), q = lane & 7;
-      const v4u v = *reinterpret_cast<const v4u *>(reg + row * 128 + ((q ^ (row & 7)) << 4));
+      v[p] = *reinterpret_cast<const v4u *>(reg + row * 128 + ((q ^ (row & 7)) << 4));
+    }
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int row = p * 8 + (lane >> 3), q = lane & 7;
       __builtin_amdgcn_raw_buffer_store_b128(
-          v, crsrc,
+          v[p], crsrc,
           static_cast<int>((static_cast<uint32_t>(wn * 64 + row) * ld + wk * 128 + c * 64 + q * 8) * 2u), 0, 2);
     }
     // the next chunk overwrites the region only after these reads (in order)
