@@ -316,7 +316,7 @@ __global__ __launch_bounds__(NTHREAD, 1) void grouped_mxfp8_kernel(
       if constexpr (EXACT)
         compute_step_bf16<XFP4>(st, acc, xrow, grow, wk, wn, l32, g);
       else
-        compute_step<XFP4>(st, acc, xrow, grow, chunk_off, wk, wn, l32, g, 0, TT);
+        compute_step<XFP4>(st, acc, xrow, grow, chunk_off, wk, wn, l32, g);
       buf ^= 1;
     }
     // ---- epilogue: C[m0 + m][j0 + j] for the tile's rows; the descriptor

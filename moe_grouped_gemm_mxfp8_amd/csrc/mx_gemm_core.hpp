@@ -52,12 +52,8 @@ __device__ __forceinline__ uint32_t tile_row4(int r) {
   return static_cast<uint32_t>(((r >> 6) * 4 + (r & 3)) * BLK4 + ((r & 63) >> 2) * TT4);
 }
 
-// Zeroes the codes of the contraction elements outside [rlo, rhi)
-// (step-relative) in a B-operand fragment of 64-element half h: dword i of lane group g holds tokens
-// 64h + 16g + 4i .. +3 (i < 4) and 64h + 32 + 16g + 4(i-4) .. +3 (i >= 4).  A
-// zero code makes the product zero, so the step then sums the expert's
-// tokens only (the weight gradient's first and last step of an expert whose
-// bounds are not multiples of 128).
+// Byte mask of a dword of codes keeping bytes j with first <= j < end (the
+// elements of an expert, relative to the dword's first element).
 __device__ __forceinline__ uint32_t keep_bytes(int first, int end) {
   // bytes j of a dword with first <= j < end, for first, end clamped to [0, 4]
   const int a = clampi(first, 0, 4), b = clampi(end, 0, 4);
@@ -65,26 +61,19 @@ __device__ __forceinline__ uint32_t keep_bytes(int first, int end) {
   const uint32_t below_a = a >= 4 ? 0xFFFFFFFFu : ((1u << (8 * a)) - 1u);
   return b > a ? (below_b & ~below_a) : 0u;
 }
-__device__ __forceinline__ void mask_tokens(v8i &frag, int h, int g, int rlo, int rhi) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int t = 64 * h + (i < 4 ? 16 * g + 4 * i : 32 + 16 * g + 4 * (i - 4));
-    frag[i] = static_cast<int>(static_cast<uint32_t>(frag[i]) & keep_bytes(rlo - t, rhi - t));
-  }
-}
 
 // One 128-step of the contraction for a wave's 128 x 64 patch: 16
 // block-scaled MFMAs.  The A-operand tile (rows =
 // output rows of the MFMA) and the B-operand tile (rows = output columns) sit
-// at ST_A and ST_B of stage st.  Contraction elements outside [rlo, rhi)
-// (step-relative) are zeroed in the B-operand fragments first.  The fragments of
+// at ST_A and ST_B of stage st (elements outside an expert already zeroed
+// by mask_stage_elements).  The fragments of
 // both 64-element halves are read from LDS up front and the MFMAs of the
 // first half are interleaved with the reads of the second, so only the first
 // reads' latency is exposed.
 template <bool XFP4 = false>
 __device__ __forceinline__ void compute_step(const uint8_t *st, v16f (&acc)[4][2], const uint32_t (&xrow)[4],
                                              const uint32_t (&grow)[2], const uint32_t (&chunk_off)[2][2],
-                                             int wk, int wn, int l32, int g, int rlo, int rhi) {
+                                             int wk, int wn, int l32, int g) {
   uint32_t sx[4], sg[2];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
@@ -125,13 +114,6 @@ __device__ __forceinline__ void compute_step(const uint8_t *st, v16f (&acc)[4][2
   for (int a = 0; a < 4; ++a) x[a] = xfrag(xrow[a], 0);
 #pragma unroll
   for (int b = 0; b < 2; ++b) g1[b] = frag(grow[b], 1);
-  if (rlo > 0 || rhi < TT) {
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      mask_tokens(g0[b], 0, g, rlo, rhi);
-      mask_tokens(g1[b], 1, g, rlo, rhi);
-    }
-  }
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
     mm(a, 0, x[a], g0[0], 0);

@@ -274,15 +274,15 @@ __global__ __launch_bounds__(NTHREAD, 1) void wgrad_mxfp8_kernel(
       }
 
       uint8_t *st = smem + buf * STAGE_BYTES;
-      if constexpr (EXACT) {
-        const int rlo = cur.lo - s * TT, rhi = cur.hi - s * TT;
-        if (rlo > 0 || rhi < TT) {             // an expert's partial first or last step
-          mask_stage_elements(st, tid, rlo, rhi);
-          barrier();
-        }
+      const int rlo = cur.lo - s * TT, rhi = cur.hi - s * TT;
+      if (rlo > 0 || rhi < TT) {               // an expert's partial first or last step
+        mask_stage_elements(st, tid, rlo, rhi);
+        barrier();
+      }
+      if constexpr (EXACT)
         compute_step_bf16(st, acc, xrow, grow, wk, wn, l32, g);
-      } else
-        compute_step(st, acc, xrow, grow, chunk_off, wk, wn, l32, g, cur.lo - s * TT, cur.hi - s * TT);
+      else
+        compute_step(st, acc, xrow, grow, chunk_off, wk, wn, l32, g);
       buf ^= 1;
     }
 
