@@ -213,6 +213,7 @@ __global__ __launch_bounds__(NTHREAD, 1) void grouped_mxfp8_kernel(
     xrow[a] = ST_A + (XFP4 ? tile_row4(wk * 128 + a * 32 + l32) : tile_row(wk * 128 + a * 32 + l32));
 #pragma unroll
   for (int bb = 0; bb < 2; ++bb) grow[bb] = ST_B + tile_row(wn * 64 + bb * 32 + l32);
+  const uint32_t growh[2] = {ST_B + tile_row(wn * 32 + l32), 0u};   // the half layout's rows
   uint32_t chunk_off[2][2];   // [half][piece] -> 16-byte chunk offset within the row
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -251,14 +252,19 @@ __global__ __launch_bounds__(NTHREAD, 1) void grouped_mxfp8_kernel(
       for (int i = 0; i < 8; ++i)
         dma_b128(srd_x, voff_t[i], cpos, __builtin_amdgcn_readfirstlane(base + ST_A + (w4 * 8 + i) * BLK));
     }
+    // a half tile (exact form, at most 128 token rows) reads token rows 0..127
+    // only: loaders 2 and 3 leave rows 128..255 and their scales unloaded
+    const bool token_rows = !(EXACT && rows <= 128u && w4 >= 2);
+    if (token_rows) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      dma_b128(srd_g, voff_t[i], cpos, __builtin_amdgcn_readfirstlane(base + ST_B + (w4 * 8 + i) * BLK));
+      for (int i = 0; i < 8; ++i)
+        dma_b128(srd_g, voff_t[i], cpos, __builtin_amdgcn_readfirstlane(base + ST_B + (w4 * 8 + i) * BLK));
+    }
     const v4i srd_sx = make_srd(SB + wrow * scale_row, 256u * scale_row);
     const v4i srd_sg = make_srd(SA + static_cast<size_t>(ld_t.m0) * scale_row, rows * scale_row);
     dma_b32(srd_sx, voff_s, cpos / 32, __builtin_amdgcn_readfirstlane(base + ST_SA + w4 * 256));
-    dma_b32(srd_sg, voff_s, cpos / 32, __builtin_amdgcn_readfirstlane(base + ST_SB + w4 * 256));
-    ops += LOADS_PER_STEP;
+    if (token_rows) dma_b32(srd_sg, voff_s, cpos / 32, __builtin_amdgcn_readfirstlane(base + ST_SB + w4 * 256));
+    ops += token_rows ? LOADS_PER_STEP : LOADS_PER_STEP - 9;
   };
   // wait until the loads of the step in buffer b have landed: every vector
   // memory instruction issued after them may still be in flight
@@ -303,26 +309,35 @@ __global__ __launch_bounds__(NTHREAD, 1) void grouped_mxfp8_kernel(
       for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[a][bb][i] = 0.f;
+    // the tile's steps; NB = 1: the half layout (all eight waves on token
+    // rows 0..127, 32 each), NB = 2: the full one
+    auto run = [&](auto nb) __attribute__((always_inline)) {
+      constexpr int NB = decltype(nb)::value;
 #pragma unroll 1
-    for (int s = 0; s < nk; ++s) {
-      wait_step(buf);
-      barrier();
-      if (ld_t.kind == 1) {
-        issue_stage(buf ^ 1);
-        mark[buf ^ 1] = ops;
-        advance();
+      for (int s = 0; s < nk; ++s) {
+        wait_step(buf);
+        barrier();
+        if (ld_t.kind == 1) {
+          issue_stage(buf ^ 1);
+          mark[buf ^ 1] = ops;
+          advance();
+        }
+        const uint8_t *st = smem + buf * STAGE_BYTES;
+        if constexpr (EXACT)
+          compute_step_bf16<XFP4, NB>(st, acc, xrow, NB == 2 ? grow : growh, wk, wn, l32, g);
+        else
+          compute_step<XFP4>(st, acc, xrow, grow, chunk_off, wk, wn, l32, g);
+        buf ^= 1;
       }
-      const uint8_t *st = smem + buf * STAGE_BYTES;
-      if constexpr (EXACT)
-        compute_step_bf16<XFP4>(st, acc, xrow, grow, wk, wn, l32, g);
-      else
-        compute_step<XFP4>(st, acc, xrow, grow, chunk_off, wk, wn, l32, g);
-      buf ^= 1;
-    }
-    // ---- epilogue: C[m0 + m][j0 + j] for the tile's rows; the descriptor
-    // drops the rest
-    store_tile(acc, smem + (buf ^ 1) * STAGE_BYTES, crsrc, Nu, wk, wn, tid);
-    ops += STORES_PER_TILE;
+      // ---- epilogue: C[m0 + m][j0 + j] for the tile's rows; the descriptor
+      // drops the rest
+      store_tile<NB>(acc, smem + (buf ^ 1) * STAGE_BYTES, crsrc, Nu, wk, wn, tid);
+      ops += STORES_PER_TILE * NB / 2;
+    };
+    if (EXACT && cur.rows <= 128)
+      run(std::integral_constant<int, 1>());
+    else
+      run(std::integral_constant<int, 2>());
   }
   wait_vmcnt<0>();
 }

@@ -211,15 +211,20 @@ __device__ __forceinline__ void mask_stage_elements(uint8_t *st, int tid, int rl
 // (their registers would spill).  An fp4 A-operand tile (XFP4) holds the
 // same 16 elements of a lane in 8 bytes (dword 0 for chunk 2j, dword 1 for
 // chunk 2j + 1).
-template <bool XFP4 = false>
+//
+// NB = 2: the wave's B-operand rows are wn*64 .. +63 (grow[0..1]); NB = 1:
+// only wn*32 .. +31 (grow[0]; accumulators acc[a][0]), the layout of a tile
+// whose B-operand rows past 128 are all empty.
+template <bool XFP4 = false, int NB = 2>
 __device__ __forceinline__ void compute_step_bf16(const uint8_t *st, v16f (&acc)[4][2], const uint32_t (&xrow)[4],
                                                   const uint32_t (&grow)[2], int wk, int wn, int l32, int g) {
-  uint32_t sx[4], sg[2];
+  uint32_t sx[4], sg[NB];
 #pragma unroll
   for (int a = 0; a < 4; ++a) sx[a] = *reinterpret_cast<const uint32_t *>(st + ST_SA + 4 * (wk * 128 + a * 32 + l32));
 #pragma unroll
-  for (int b = 0; b < 2; ++b) sg[b] = *reinterpret_cast<const uint32_t *>(st + ST_SB + 4 * (wn * 64 + b * 32 + l32));
-  auto read = [&](int j, v4u (&xr)[4], v4u (&gr)[2]) {
+  for (int b = 0; b < NB; ++b)
+    sg[b] = *reinterpret_cast<const uint32_t *>(st + ST_SB + 4 * (wn * 32 * NB + b * 32 + l32));
+  auto read = [&](int j, v4u (&xr)[4], v4u (&gr)[NB]) {
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       if constexpr (XFP4) {
@@ -230,38 +235,38 @@ __device__ __forceinline__ void compute_step_bf16(const uint8_t *st, v16f (&acc)
       }
     }
 #pragma unroll
-    for (int b = 0; b < 2; ++b) gr[b] = *reinterpret_cast<const v4u *>(st + grow[b] + 32 * j + 16 * g);
+    for (int b = 0; b < NB; ++b) gr[b] = *reinterpret_cast<const v4u *>(st + grow[b] + 32 * j + 16 * g);
   };
-  v4u xr[4], gr[2];
+  v4u xr[4], gr[NB];
   read(0, xr, gr);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    v4u xn[4], gn[2];
+    v4u xn[4], gn[NB];
     if (j < 3) read(j + 1, xn, gn);
-    float fx[4], fg[2];
+    float fx[4], fg[NB];
 #pragma unroll
     for (int a = 0; a < 4; ++a) fx[a] = e8m0_f32(sx[a], j);
 #pragma unroll
-    for (int b = 0; b < 2; ++b) fg[b] = e8m0_f32(sg[b], j);
+    for (int b = 0; b < NB; ++b) fg[b] = e8m0_f32(sg[b], j);
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      bf16x8 xa[4], gb[2];
+      bf16x8 xa[4], gb[NB];
 #pragma unroll
       for (int a = 0; a < 4; ++a)
         xa[a] = XFP4 ? cvt8_fp4(xr[a][q], fx[a]) : cvt8(xr[a][2 * q], xr[a][2 * q + 1], fx[a]);
 #pragma unroll
-      for (int b = 0; b < 2; ++b) gb[b] = cvt8(gr[b][2 * q], gr[b][2 * q + 1], fg[b]);
+      for (int b = 0; b < NB; ++b) gb[b] = cvt8(gr[b][2 * q], gr[b][2 * q + 1], fg[b]);
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < NB; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[a], gb[b], acc[a][b], 0, 0, 0);
     }
     if (j < 3) {
 #pragma unroll
       for (int a = 0; a < 4; ++a) xr[a] = xn[a];
 #pragma unroll
-      for (int b = 0; b < 2; ++b) gr[b] = gn[b];
+      for (int b = 0; b < NB; ++b) gr[b] = gn[b];
     }
     // keep the scheduler from hoisting later blocks' reads (register pressure)
     __builtin_amdgcn_sched_barrier(0);
@@ -283,6 +288,9 @@ constexpr int STORES_PER_TILE = 16;           // 16-byte stores per lane per out
 // workgroup barrier in all: a wave's LDS writes and reads of its own region
 // execute in order.  (Staging the tile in two halves shared by all waves,
 // with four barriers, measured 2-3% slower end to end.)
+// NB = 1: the half layout of compute_step_bf16 (the wave's output rows
+// wn*32 .. +31, accumulators acc[a][0]; eight stores per lane).
+template <int NB = 2>
 __device__ __forceinline__ void store_tile(const v16f (&acc)[4][2], uint8_t *stg, __amdgpu_buffer_rsrc_t crsrc,
                                            uint32_t ld, int wk, int wn, int tid) {
   // recompute the lane coordinates here rather than keep them live across
@@ -299,7 +307,7 @@ __device__ __forceinline__ void store_tile(const v16f (&acc)[4][2], uint8_t *stg
 #pragma unroll
     for (int a2 = 0; a2 < 2; ++a2)
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
+      for (int b = 0; b < NB; ++b) {
         const int rl = b * 32 + el32;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -313,18 +321,19 @@ __device__ __forceinline__ void store_tile(const v16f (&acc)[4][2], uint8_t *stg
     asm volatile("" ::: "memory");
     // all eight row pieces first, then the stores: one LDS round trip per
     // chunk instead of one per store
-    v4u v[8];
+    constexpr int NP = 4 * NB;                 // eight rows per piece, 32 NB rows
+    v4u v[NP];
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
+    for (int p = 0; p < NP; ++p) {
       const int row = p * 8 + (lane >> 3), q = lane & 7;
       v[p] = *reinterpret_cast<const v4u *>(reg + row * 128 + ((q ^ (row & 7)) << 4));
     }
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
+    for (int p = 0; p < NP; ++p) {
       const int row = p * 8 + (lane >> 3), q = lane & 7;
       __builtin_amdgcn_raw_buffer_store_b128(
           v[p], crsrc,
-          static_cast<int>((static_cast<uint32_t>(wn * 64 + row) * ld + wk * 128 + c * 64 + q * 8) * 2u), 0, 2);
+          static_cast<int>((static_cast<uint32_t>(wn * 32 * NB + row) * ld + wk * 128 + c * 64 + q * 8) * 2u), 0, 2);
     }
     // the next chunk overwrites the region only after these reads (in order)
     asm volatile("" ::: "memory");
