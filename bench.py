@@ -22,6 +22,7 @@ import hashlib
 import json
 import os
 import platform
+import re
 import sys
 import time
 
@@ -54,11 +55,19 @@ KERNEL_NAMES = {"wgrad": "wgrad_mxfp8_kernel", "dgrad": "dgrad_f32_kernel", "qua
                 "forward": "grouped_mxfp8_kernel", "a8w4": "grouped_mxfp8_kernel"}
 
 
+def code_text(src: str) -> str:
+    """A kernel source without its comments, trailing blanks and empty lines, so
+    that comment edits do not mark a measured kernel as changed."""
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    lines = (re.sub(r"//.*", "", line).rstrip() for line in src.splitlines())
+    return "\n".join(line for line in lines if line)
+
+
 def source_digest(pass_name: str) -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[pass_name]:
-        with open(os.path.join(ROOT, "moe_grouped_gemm_mxfp8_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "moe_grouped_gemm_mxfp8_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(code_text(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -1,7 +1,7 @@
 // Grouped MXFP8 weight gradient on gfx950:
 //   grad_w[e*N + n][k] = sum over tokens m of expert e of  g^T[n][m] x^T[k][m]
-// with E4M3 elements and one E8M0 scale per 32 tokens, f32 accumulation in
-// the block-scaled MFMA, bf16 output (the tinygrad page "grouped_mxfp8_wgrad.cpp":
+// with E4M3 elements and one E8M0 scale per 32 tokens, f32 accumulation,
+// bf16 output (the tinygrad page "grouped_mxfp8_wgrad.cpp":
 // its global layouts, the per-expert 128-token k-loop and the epilogue).
 //
 // Design (gfx950):
@@ -27,6 +27,10 @@
 //    block, eight lanes per row reading the row's 128 bytes in order (whole
 //    lines, no permuted lanes), and rows are placed so that the 16 rows an
 //    MFMA operand read touches at once fall on 16 distinct bank groups.
+//    An expert whose bounds are not multiples of 128 has a partial first and
+//    last step: before those steps' MFMAs all 512 threads zero the staged
+//    g^T codes of the tokens outside the expert (one pass over the tile and
+//    one more barrier), so the step code itself never masks.
 //  * 8 waves as 2 (k) x 4 (n); each wave owns a 128 (k) x 64 (n) output
 //    patch as 4 x 2 accumulators of 32 x 32 MFMA results.  x^T is the MFMA A
 //    operand (rows = k) and g^T the B operand (columns = n).
