@@ -114,7 +114,20 @@ def blas_threads():
     return os.cpu_count() or 1
 
 
+LAUNCH_DIST = {}     # per-launch times of the last timed region (ms): median, p10, p90
+
+
+def quantiles(ms_list):
+    q = sorted(ms_list)
+    pick = lambda f: q[int(round(f * (len(q) - 1)))]
+    return {"median": round(pick(0.5), 4), "p10": round(pick(0.1), 4), "p90": round(pick(0.9), 4), "n": len(q)}
+
+
 def time_steps(torch, fn, steps, warmup):
+    """W untimed warm-ups, then exactly K timed launches on torch's current stream
+    (the stream the library launches on), bracketed by two events.  Afterwards,
+    outside the timed region, K more launches with an event between each give
+    the per-launch distribution."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -126,7 +139,34 @@ def time_steps(torch, fn, steps, warmup):
         fn()
     stop.record(stream)
     torch.cuda.synchronize()
-    return start.elapsed_time(stop) / steps  # ms per step
+    ms = start.elapsed_time(stop) / steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        fn()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    LAUNCH_DIST.clear()
+    LAUNCH_DIST.update(quantiles([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]))
+    return ms  # ms per step of the timed region
+
+
+def time_cold(torch, fn, reps=20, scratch_bytes=512 << 20):
+    """Each launch timed alone after a 512 MB write that evicts L2 and the MALL."""
+    d = torch.device("cuda:0")
+    scratch = torch.empty(scratch_bytes, dtype=torch.uint8, device=d)
+    stream = torch.cuda.current_stream()
+    out = []
+    for r in range(reps):
+        scratch.fill_(r & 0xFF)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1))
+    del scratch
+    return quantiles(out)
 
 
 def bind_roofline(line, flop, nbytes, ms):
@@ -182,6 +222,9 @@ def bench_wgrad(torch, mg, idx, steps, warmup, cpu_baseline, fast=False):
     # the aligned 2048^3 and the 64-expert workloads: the bf16 output's stores
     # outweigh the MFMA work
     bind_roofline(line, flop, algo_bytes, ms)
+    if idx == 3:
+        # also cold: each launch alone after a 512 MB write (L2 and MALL evicted)
+        line["cold_ms"] = time_cold(torch, lambda: mg.wgrad_mxfp8(qa, qb, sa, sb, off, out=out, fast=fast))
     if cpu_baseline:
         line["cpu_baseline"] = cpu_wgrad_baseline(inp)
     return line
@@ -471,6 +514,8 @@ def main():
                  "data": "synthetic (seeded numpy generators, workload recipe)",
                  "kernel": KERNEL_NAMES.get(args.pass_name, "torch copy"),
                  "kernel_source_digest": source_digest(args.pass_name) if args.pass_name in KERNEL_SOURCES else None})
+    if LAUNCH_DIST:
+        line["per_launch_ms"] = dict(LAUNCH_DIST)
     print(json.dumps(line), flush=True)
 
 
