@@ -69,6 +69,31 @@ def test_wgrad_small(name):
             assert np.all(blk == 0) and not np.any(np.signbit(blk))
 
 
+BOUNDS = [1, 2, 3, 4, 5, 31, 32, 33, 63, 64, 65, 95, 96, 97, 126, 127, 129, 191, 255]
+
+
+@pytest.mark.parametrize("fast", [False, True])
+def test_wgrad_every_bound_position(fast):
+    """Two experts over 384 tokens, split at token b for b at every byte position
+    of a dword and on both sides of the 32-, 64- and 128-token lines: the partial
+    steps zero the other expert's codes in the staged tile before the MFMAs.
+    Default entry point against the oracle, fast one against the hardware model."""
+    import hw_mfma_model as hw
+    torch, mg = require_gpu()
+    N, K, M = 256, 256, 384
+    rng = np.random.default_rng(23)
+    gT = rng.standard_normal((N, M)).astype(np.float32)
+    xT = rng.standard_normal((K, M)).astype(np.float32)
+    gT[rng.random(gT.shape) < 0.01] *= 64
+    ca, sa, cb, sb = _mx_inputs(gT, xT)
+    say("wgrad every bound position", "fast" if fast else "exact")
+    for b in BOUNDS:
+        off = np.array([0, b, M], np.int32)
+        got = (_run_fast if fast else _run)(torch, mg, ca, sa, cb, sb, off)
+        ref = hw.wgrad_one_pass(ca, sa, cb, sb, off) if fast else oracle.wgrad(ca, sa, cb, sb, off)
+        assert oracle.wgrad_excess(got, ref) <= 0, (b, oracle.wgrad_excess(got, ref))
+
+
 def test_wgrad_all_ones_is_exact():
     torch, mg = require_gpu()
     counts = [384, 0, 1152, 128]
