@@ -208,7 +208,7 @@ def bench_wgrad(torch, mg, idx, steps, warmup, cpu_baseline, fast=False):
         "ms_per_step": round(ms, 4),
         "dtype": "fp8e4m3*fp8e4m3->f32 acc, bf16 out" if fast else "mxfp8 (e4m3+e8m0) -> bf16 MFMA, f32 acc, bf16 out",
         "mode": "block-scaled fp8 MFMA (hardware run-of-8 rounding)" if fast
-        else "E4M3 x E8M0 converted exactly to bf16, bf16 MFMA (exact-sum accuracy)",
+        else "E4M3 x E8M0 converted exactly to bf16, bf16 MFMA (exact sum up to f32-level accumulation error)",
         "config": {"workload": w.name, "E": w.E, "M": w.M, "N": w.N, "K": w.K,
                    "tokens_per_expert": [int(c) for c in np.diff(off_np)]},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_FP8_TFLOPS,

@@ -93,11 +93,13 @@ enum {
  * of the codes into two passes avoids it (several outliers of one row can
  * share a run).  This entry point therefore converts the codes, times their
  * scales, to bf16 (exactly: 4 significant bits, the scale inside bf16's
- * exponent range) and multiplies them on the bf16 MFMA, which adds its
- * products without that truncation; the accumulator is f32.  The result is
- * the exact sum up to f32 accumulation and the final bf16 rounding, on any
- * input.  Scale bytes below 2^-126 relative to the codes' range (results
- * below bf16's normal range) are flushed by the conversion.
+ * exponent range) and multiplies them on the bf16 MFMA, which adds its 16
+ * products to within 2^-22 of the largest of them (measured; the exact sum,
+ * rounded once, when they span 2^14 or less) into the f32 accumulator.  The
+ * result is thus the exact sum up to f32-level accumulation error and the
+ * final bf16 rounding, with or without outliers.  Scale bytes below 2^-126
+ * relative to the codes' range (results below bf16's normal range) are
+ * flushed by the conversion.
  */
 MOE_GG_API int moe_gg_wgrad_mxfp8(const uint8_t *A, const uint8_t *B, uint16_t *C,
                                   const uint8_t *scale_A, const uint8_t *scale_B,
@@ -174,8 +176,8 @@ MOE_GG_API int moe_gg_dgrad_f32(const float *A, const float *B, float *C,
  * K % 128 == 0 and E <= 2048 (EUNSUPPORTED otherwise).  Accuracy as for the
  * weight gradient: the codes, times their scales, are converted exactly to
  * bf16 and multiplied on the bf16 MFMA with f32 accumulation, so the result
- * is the exact sum up to f32 accumulation and the bf16 rounding on any input
- * (outliers in either operand or both).
+ * is the exact sum up to f32-level accumulation error and the bf16 rounding,
+ * also with outliers in either operand or both.
  */
 MOE_GG_API int moe_gg_grouped_mxfp8(const uint8_t *A, const uint8_t *B, uint16_t *C,
                                     const uint8_t *scale_A, const uint8_t *scale_B,

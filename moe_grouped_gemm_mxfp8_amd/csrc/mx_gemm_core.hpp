@@ -140,9 +140,10 @@ __device__ __forceinline__ void compute_step(const uint8_t *st, v16f (&acc)[4][2
 // products of every run of 8 contraction elements to 2^(largest exponent sum
 // of the run - 13) (measured; the products of one run are not added exactly),
 // so where an outlier of one operand meets an outlier of the other at the
-// same token, the run's other products are lost.  The bf16 MFMA adds its
-// products without that truncation (measured: 2^20 + 15 ones, and fractions
-// down to 2^-6 next to 4096, come out exact).  An E4M3 code times its E8M0
+// same token, the run's other products are lost.  The bf16 MFMA adds its 16
+// products to within 2^-22 of the largest (measured: 2^20 + 15 ones come out
+// exact, and products spanning 2^14 give the exact sum rounded once), the
+// error of an f32 accumulation.  An E4M3 code times its E8M0
 // scale is exactly a bf16 (3 mantissa bits of 7, the scale inside bf16's
 // exponent range), so this step converts the fragments with
 // v_cvt_scalef32_pk_bf16_fp8 (two codes per instruction, the block's scale

@@ -32,8 +32,8 @@ _U8 = (torch.uint8, torch.float8_e4m3fn, torch.float8_e8m0fnu) if hasattr(torch,
 def wgrad_mxfp8(a, b, scale_a, scale_b, expert_off, out=None, fast=False):
     """grad_w[E*N, K] (bf16) from g^T codes a[N, M], x^T codes b[K, M], E8M0 scales [.., M/32].
 
-    fast=False: bf16 MFMAs on the exactly converted MX operands (the exact sum up to f32
-    accumulation and the bf16 rounding).
+    fast=False: bf16 MFMAs on the exactly converted MX operands (the exact sum up to
+    f32-level accumulation error and the bf16 rounding).
     fast=True: the block-scaled fp8 MFMA with the hardware's 8-token truncating reduction.
     """
     _dev(a, "a", _U8); _dev(b, "b", _U8)

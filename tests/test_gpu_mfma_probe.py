@@ -257,3 +257,104 @@ def test_scaled_mfma_run_rule_by_hand(probe):
     _, o32 = probe(a, b, unit, unit)
     for c, (_, want) in enumerate(cases):
         assert _unpack(32, o32[c, 0])[0, 0] == want, (c, _unpack(32, o32[c, 0])[0, 0], want)
+
+
+# ---- v_mfma_f32_32x32x16_bf16: the instruction of the exact entry points ----
+
+def _bf16_bits(vals):
+    """bf16 bit patterns of values that bf16 holds exactly."""
+    v = np.asarray(vals, np.float32)
+    bits = v.view(np.uint32)
+    assert np.all(bits & 0xFFFF == 0), "value not exact in bf16"
+    return (bits >> 16).astype(np.uint16)
+
+
+@pytest.fixture(scope="module")
+def bf16_probe():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    if not os.path.exists(LIB):
+        pytest.fail(f"probe library not built: {LIB} (run __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB)
+    lib.bf16_probe_run.restype = ctypes.c_int
+    lib.bf16_probe_run.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int, ctypes.c_void_p]
+
+    def run(a_vals, b_vals):
+        """a_vals, b_vals: [n, 64 lanes, 8] values; returns D [n, 32, 32] (rows from A's lanes)."""
+        n = a_vals.shape[0]
+        dev = torch.device("cuda:0")
+        A = torch.from_numpy(_bf16_bits(a_vals).reshape(n, 64, 8).view(np.int32).copy()).to(dev)
+        B = torch.from_numpy(_bf16_bits(b_vals).reshape(n, 64, 8).view(np.int32).copy()).to(dev)
+        out = torch.empty(n * 64 * 16, dtype=torch.float32, device=dev)
+        assert lib.bf16_probe_run(A.data_ptr(), B.data_ptr(), out.data_ptr(), n,
+                                  torch.cuda.current_stream().cuda_stream) == 0
+        torch.cuda.synchronize()
+        regs = out.cpu().numpy().reshape(n, 64, 16).astype(np.float64)
+        return np.stack([_unpack(32, regs[i]) for i in range(n)])
+    return run
+
+
+def _bf16_model(a_vals, b_vals):
+    """D[r][c] = sum over lane group g and element i of A(lane r + 32g)[i] * B(lane c + 32g)[i],
+    in exact rational arithmetic (fp64 holds every case below exactly)."""
+    a = np.concatenate([a_vals[:32], a_vals[32:]], axis=1)      # [32 rows, 16]
+    b = np.concatenate([b_vals[:32], b_vals[32:]], axis=1)
+    return a.astype(np.float64) @ b.astype(np.float64).T
+
+
+def test_bf16_mfma_layout_small_integers(bf16_probe):
+    rng = np.random.default_rng(5)
+    a = rng.integers(-4, 5, (3, 64, 8)).astype(np.float32)
+    b = rng.integers(-4, 5, (3, 64, 8)).astype(np.float32)
+    got = bf16_probe(a, b)
+    for i in range(3):
+        assert np.array_equal(got[i], _bf16_model(a[i], b[i]))
+
+
+def test_bf16_mfma_adds_products_without_run_truncation(bf16_probe):
+    """A row [2^20, 1 x 15] against ones gives 2^20 + 15, and [4096, 2^-6 x 15] gives
+    4096 + 15/64: products 2^20 (and 2^18) below the largest are kept, where the block-
+    scaled fp8 MFMA keeps 13 bits below its largest exponent sum per run of 8."""
+    for big, small in ((2.0 ** 20, 1.0), (4096.0, 2.0 ** -6)):
+        a = np.full((1, 64, 8), small, np.float32)
+        a[0, :32, 0] = big                                      # lane group 0, element 0 of every row
+        b = np.ones((1, 64, 8), np.float32)
+        got = bf16_probe(a, b)[0]
+        assert np.all(got == big + 15 * small), (big, small, np.unique(got))
+
+
+def test_bf16_mfma_error_relative_to_largest_product(bf16_probe):
+    """Values m 2^e with 4 significant bits (the class an E4M3 code times its E8M0
+    scale falls in).  With e in [-10, 10] (products spanning ~2^40) every result is
+    within 2^-21 of the largest of its 16 products; with e in [-3, 3] every result is
+    the exact sum rounded once to f32."""
+    rng = np.random.default_rng(11)
+    n = 8
+    def draw(lo, hi):
+        m = rng.integers(8, 16, (n, 64, 8)) / 8.0
+        e = rng.integers(lo, hi + 1, (n, 64, 8))
+        s = np.where(rng.random((n, 64, 8)) < 0.5, -1.0, 1.0)
+        return (s * m * np.exp2(e)).astype(np.float32)
+    for lo, hi in ((-10, 10), (-3, 3)):
+        a, b = draw(lo, hi), draw(lo, hi)
+        got = bf16_probe(a, b)
+        worst_rel, exact_rounded, total = 0.0, 0, 0
+        for i in range(n):
+            ref = _bf16_model(a[i], b[i])                   # exact: spans < 53 bits
+            A = np.concatenate([a[i][:32], a[i][32:]], axis=1).astype(np.float64)
+            B = np.concatenate([b[i][:32], b[i][32:]], axis=1).astype(np.float64)
+            pmax = np.max(np.abs(A[:, None, :] * B[None, :, :]), axis=-1)
+            worst_rel = max(worst_rel, float(np.max(np.abs(got[i] - ref) / pmax)))
+            rn = ref.astype(np.float32).astype(np.float64)
+            exact_rounded += int(np.sum(got[i] == rn))
+            total += got[i].size
+        lg = np.log2(worst_rel) if worst_rel > 0 else float("-inf")
+        print(f"bf16 MFMA, exponents [{lo}, {hi}]: {exact_rounded}/{total} correctly rounded; "
+              f"worst error 2^{lg:.2f} of the largest product", flush=True)
+        # measured on gfx950: within 2^-22 of the largest product over a ~2^40 span
+        # (f32-accumulation level, not the exact sum), and the exact sum rounded once
+        # to f32 when the products span 2^14
+        assert worst_rel <= 2.0 ** -21, (lo, hi, worst_rel)
+        if hi - lo <= 6:
+            assert exact_rounded == total, (lo, hi, exact_rounded, total)
