@@ -20,8 +20,12 @@
 //    instead of 2).
 //  * The contraction runs in chunks of 32 n.  g[128 x 32] and W_e[32 x 128]
 //    are read with 16-byte coalesced loads (g rows and W rows are contiguous
-//    along n and k) into registers, then written to a double-buffered LDS
+//    along n and k) into registers, one chunk ahead (two for a pass over
+//    fewer than four row blocks), then written to a double-buffered LDS
 //    stage while the previous chunk is multiplied.
+//  * One-dimensional grid in an XCD-aware order: the tiles one XCD runs at
+//    once form a patch of row tiles x 8 column tiles sharing g rows and W
+//    columns in that XCD's L2.
 //  * Inside a chunk the MFMA k index s = 0..15 of lane group h = l/32 is
 //    n = 16h + s, so each lane reads its 16 g values with 4 ds_read_b128.  g
 //    rows in LDS are 128 bytes with their 16-byte groups XOR-swizzled by
@@ -37,6 +41,7 @@ constexpr int BM = 128;      // rows per tile
 constexpr int BK = 128;      // output columns (k) per tile
 constexpr int BC = 32;       // contraction (n) per chunk
 constexpr int NTHREAD = 256;
+constexpr int XGROUP = 8;    // column tiles per group of the XCD-aware tile order
 
 constexpr int LG = 0;                    // g chunk   [128][32] f32 = 16 KB
 constexpr int LW = BM * BC * 4;          // W chunk   [32][128] f32 = 16 KB
@@ -51,16 +56,19 @@ __device__ __forceinline__ uint32_t w_lds_off(int n, int col /*float index*/) {
 
 // One expert pass over a tile: rows [lo, hi) of expert e (W_e = We), which lie
 // in the NRB 32-row blocks ib0 .. ib0 + NRB - 1 of the tile; the whole
-// contraction in chunks of 32 n, double-buffered through LDS, then the pass's
-// rows stored.  Every wave runs it (it contains the workgroup's barriers).
+// contraction in chunks of 32 n, loaded ahead into registers and
+// double-buffered through LDS, then the pass's rows stored.  Every wave runs
+// it (it contains the workgroup's barriers).
 template <int NRB>
 __device__ __forceinline__ void dgrad_pass(const float *__restrict__ G, const float *__restrict__ We,
                                            float *__restrict__ DX, uint8_t *smem, int M, int N, int K, int r0,
                                            int k0, int lo, int hi, int ib0, int tid, int wave) {
   const int lane = tid & 63;
   const int h = lane >> 5, l32 = lane & 31;
-  // global -> register loader coordinates (4 float4 of g and 4 of W per thread)
-  const int g_row = tid >> 3, g_q = tid & 7;      // rows g_row + 32i, group g_q
+  // global -> register loader coordinates (NRB float4 of g and 4 of W per
+  // thread; only the pass's row blocks are loaded and staged, the MFMAs read
+  // no other rows)
+  const int g_row = tid >> 3, g_q = tid & 7;      // rows g_row + 32(ib0 + j), group g_q
   const int w_n = tid >> 5, w_q = tid & 31;       // n rows w_n + 8i, float4 column w_q
   const int nchunks = (N + BC - 1) / BC;
 
@@ -70,63 +78,92 @@ __device__ __forceinline__ void dgrad_pass(const float *__restrict__ G, const fl
 #pragma unroll
     for (int x = 0; x < 16; ++x) acc[i][x] = 0.f;
 
-  v4f greg[4], wreg[4];
-  auto load_chunk = [&](int c) __attribute__((always_inline)) {
+  // Chunks are loaded DEPTH ahead into registers.  A pass with fewer than four
+  // row blocks (little MFMA work per chunk) keeps two register sets: chunk
+  // c + 2 is loaded while chunk c multiplies and chunk c + 1 waits in the
+  // other set, so the global load latency has two chunks of MFMA time to hide
+  // behind.  A full pass loads one chunk ahead (a second set would not fit
+  // beside its accumulators in 256 VGPRs).
+  constexpr int DEPTH = NRB < 4 ? 2 : 1;
+  v4f greg[DEPTH][NRB], wreg[DEPTH][4];
+  auto load_chunk = [&](int c, int set) __attribute__((always_inline)) {
     const int n0 = c * BC;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = r0 + g_row + 32 * i;
+    for (int j = 0; j < NRB; ++j) {
+      const int r = r0 + g_row + 32 * (ib0 + j);
       const int n = n0 + 4 * g_q;
       if (r >= lo && r < hi && n < N)
-        greg[i] = *reinterpret_cast<const v4f *>(G + static_cast<size_t>(r) * N + n);
+        greg[set][j] = *reinterpret_cast<const v4f *>(G + static_cast<size_t>(r) * N + n);
       else
-        greg[i] = (v4f){0.f, 0.f, 0.f, 0.f};
+        greg[set][j] = (v4f){0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int n = n0 + w_n + 8 * i;
       const int k = k0 + 4 * w_q;
       if (n < N && k < K)
-        wreg[i] = *reinterpret_cast<const v4f *>(We + static_cast<size_t>(n) * K + k);
+        wreg[set][i] = *reinterpret_cast<const v4f *>(We + static_cast<size_t>(n) * K + k);
       else
-        wreg[i] = (v4f){0.f, 0.f, 0.f, 0.f};
+        wreg[set][i] = (v4f){0.f, 0.f, 0.f, 0.f};
     }
   };
-  auto store_chunk = [&](int buf) __attribute__((always_inline)) {
+  auto store_chunk = [&](int set, int buf) __attribute__((always_inline)) {
     uint8_t *st = smem + buf * STAGE;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<v4f *>(st + g_lds_off(g_row + 32 * i, g_q)) = greg[i];
+    for (int j = 0; j < NRB; ++j)
+      *reinterpret_cast<v4f *>(st + g_lds_off(g_row + 32 * (ib0 + j), g_q)) = greg[set][j];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<v4f *>(st + w_lds_off(w_n + 8 * i, 4 * w_q)) = wreg[i];
+      *reinterpret_cast<v4f *>(st + w_lds_off(w_n + 8 * i, 4 * w_q)) = wreg[set][i];
   };
 
-  load_chunk(0);
-  store_chunk(0);
-  barrier();
-  for (int c = 0; c < nchunks; ++c) {
-    const int buf = c & 1;
-    if (c + 1 < nchunks) load_chunk(c + 1);
-    const uint8_t *st = smem + buf * STAGE;
-    // this lane's 16 g values per row block: n = 16h .. 16h+15
-    v4f ga[NRB][4];
+  // chunk c (c % 2 = P) multiplies from LDS buffer P
+  auto chunk = [&](int c, auto parity) __attribute__((always_inline)) {
+    constexpr int P = decltype(parity)::value;
+    constexpr int LOAD_SET = DEPTH == 2 ? P : 0, NEXT_SET = DEPTH == 2 ? (P ^ 1) : 0;
+    if (c + DEPTH < nchunks) load_chunk(c + DEPTH, LOAD_SET);
+    const uint8_t *st = smem + P * STAGE;
+    // this lane's 16 n values n = 16h .. 16h+15 in four groups of four: group
+    // q's g values (one 16-byte read per row block) and W values are read
+    // while group q - 1 multiplies, into a second register set
+    v4f ga[2][NRB];
+    float wv[2][4];
+    auto read_group = [&](int q, v4f (&gq)[NRB], float (&wq)[4]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < NRB; ++i) {
-      const int row = (ib0 + i) * 32 + l32;
+      for (int i = 0; i < NRB; ++i) gq[i] = *reinterpret_cast<const v4f *>(st + g_lds_off((ib0 + i) * 32 + l32, 4 * h + q));
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        ga[i][q] = *reinterpret_cast<const v4f *>(st + g_lds_off(row, 4 * h + q));
+      for (int t = 0; t < 4; ++t)
+        wq[t] = *reinterpret_cast<const float *>(st + w_lds_off(16 * h + 4 * q + t, wave * 32 + l32));
+    };
+    read_group(0, ga[0], wv[0]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (q < 3) read_group(q + 1, ga[(q + 1) & 1], wv[(q + 1) & 1]);
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < NRB; ++i)
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(ga[q & 1][i][t], wv[q & 1][t], acc[i], 0, 0, 0);
+      // the next group's reads ahead of this group's MFMAs, and no later
+      // group's reads hoisted above them
+      if (q < 3) {
+        __builtin_amdgcn_sched_group_barrier(0x100, NRB + 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 4 * NRB, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      const float wb = *reinterpret_cast<const float *>(st + w_lds_off(16 * h + s, wave * 32 + l32));
-#pragma unroll
-      for (int i = 0; i < NRB; ++i)
-        acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(ga[i][s >> 2][s & 3], wb, acc[i], 0, 0, 0);
-    }
-    if (c + 1 < nchunks) store_chunk(buf ^ 1);
+    if (c + 1 < nchunks) store_chunk(NEXT_SET, P ^ 1);
     barrier();
+  };
+
+  load_chunk(0, 0);
+  if (DEPTH == 2 && nchunks > 1) load_chunk(1, DEPTH - 1);
+  store_chunk(0, 0);
+  barrier();
+#pragma unroll 1
+  for (int c = 0; c < nchunks; c += 2) {
+    chunk(c, std::integral_constant<int, 0>());
+    if (c + 1 < nchunks) chunk(c + 1, std::integral_constant<int, 1>());
   }
 
   // this pass's rows: register x of acc[i] is row (ib0 + i)*32 + 8(x/4) + 4h +
@@ -150,8 +187,22 @@ __global__ __launch_bounds__(NTHREAD, 2) void dgrad_f32_kernel(
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // column strip 32 wave .. +31
-  const int r0 = blockIdx.y * BM;
-  const int k0 = blockIdx.x * BK;
+  // Tile of this workgroup.  Workgroup b runs on XCD b mod 8, so with the
+  // tile count T a multiple of 8 the workgroups of one XCD take the
+  // contiguous range u = (b mod 8) T/8 + b/8 of a grouped order: groups of
+  // XGROUP column tiles, row-major inside a group.  The tiles one XCD runs
+  // at once then form a patch of about 64/XGROUP row tiles x XGROUP column
+  // tiles, which share g rows and W columns in that XCD's L2 (column tiles
+  // alone would give each XCD every g row).
+  const int tilesR = (M + BM - 1) / BM, tilesC = (K + BK - 1) / BK;
+  const int T = tilesR * tilesC;
+  const int b = blockIdx.x;
+  const int u = (T & 7) == 0 ? (b & 7) * (T >> 3) + (b >> 3) : b;
+  const int grp = u / (tilesR * XGROUP);
+  const int gw = min(XGROUP, tilesC - grp * XGROUP);
+  const int w = u - grp * tilesR * XGROUP;
+  const int r0 = (w / gw) * BM;
+  const int k0 = (grp * XGROUP + w % gw) * BK;
   const int r_last = min(r0 + BM, M) - 1;
   const int e_first = __builtin_amdgcn_readfirstlane(expert_of_row(off, E, r0));
   const int e_last = __builtin_amdgcn_readfirstlane(expert_of_row(off, E, r_last));
@@ -203,9 +254,10 @@ extern "C" MOE_GG_API int moe_gg_dgrad_f32(const float *A, const float *B, float
   if (!C || (N > 0 && (!A || !B))) return MOE_GG_EINVAL;
   if (K % 4 || N % 4) return MOE_GG_EUNSUPPORTED;
   if (const int st = check_offsets_if_asked(expert_off, E, M, stream)) return st;
-  const dim3 grid((K + BK - 1) / BK, (M + BM - 1) / BM);
-  if (grid.y > 65535u) return MOE_GG_EUNSUPPORTED;
-  hipLaunchKernelGGL(dgrad_f32_kernel, grid, dim3(NTHREAD), 0, stream, A, B, C, expert_off, M, N, K, E);
+  const int64_t tiles = static_cast<int64_t>((K + BK - 1) / BK) * ((M + BM - 1) / BM);
+  if (tiles > 0x7FFFFFFF) return MOE_GG_EUNSUPPORTED;
+  hipLaunchKernelGGL(dgrad_f32_kernel, dim3(static_cast<uint32_t>(tiles)), dim3(NTHREAD), 0, stream, A, B, C,
+                     expert_off, M, N, K, E);
   return hipGetLastError() == hipSuccess ? MOE_GG_OK : MOE_GG_ELAUNCH;
 }
 
