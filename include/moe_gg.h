@@ -97,9 +97,13 @@ enum {
  * products to within 2^-22 of the largest of them (measured; the exact sum,
  * rounded once, when they span 2^14 or less) into the f32 accumulator.  The
  * result is thus the exact sum up to f32-level accumulation error and the
- * final bf16 rounding, with or without outliers.  Scale bytes below 2^-126
- * relative to the codes' range (results below bf16's normal range) are
- * flushed by the conversion.
+ * final bf16 rounding, with or without outliers.  The conversion is exact
+ * for every element value bf16 can hold: any code with scale bytes 3..246
+ * (all MX quantiser outputs whose block maximum is at least 2^-116), and
+ * larger scale bytes with codes below 2^8.  Beyond that, values below
+ * bf16's smallest subnormal, 2^-133, round to multiples of it (2^-136 to
+ * zero), and values above its largest finite value become infinite
+ * (measured); the fast entry point has neither limit.
  */
 MOE_GG_API int moe_gg_wgrad_mxfp8(const uint8_t *A, const uint8_t *B, uint16_t *C,
                                   const uint8_t *scale_A, const uint8_t *scale_B,
@@ -175,9 +179,10 @@ MOE_GG_API int moe_gg_dgrad_f32(const float *A, const float *B, float *C,
  * writes +0.0 everywhere); N % 256 == 0,
  * K % 128 == 0 and E <= 2048 (EUNSUPPORTED otherwise).  Accuracy as for the
  * weight gradient: the codes, times their scales, are converted exactly to
- * bf16 and multiplied on the bf16 MFMA with f32 accumulation, so the result
- * is the exact sum up to f32-level accumulation error and the bf16 rounding,
- * also with outliers in either operand or both.
+ * bf16 (within the range stated there) and multiplied on the bf16 MFMA with
+ * f32 accumulation, so the result is the exact sum up to f32-level
+ * accumulation error and the bf16 rounding, also with outliers in either
+ * operand or both.
  */
 MOE_GG_API int moe_gg_grouped_mxfp8(const uint8_t *A, const uint8_t *B, uint16_t *C,
                                     const uint8_t *scale_A, const uint8_t *scale_B,
@@ -214,8 +219,9 @@ MOE_GG_API int moe_gg_grouped_mxfp8_fast(const uint8_t *A, const uint8_t *B, uin
  *
  * The MoE forward y = x W_e^T with A = MX(x) along K and B[e] = MXFP4(W_e)
  * along K.  Shapes, status codes and accuracy as moe_gg_grouped_mxfp8 (an
- * E2M1 value times its E8M0 scale is exactly a bf16 too); the _fast entry
- * point makes one block-scaled MFMA pass with format 4 for B.
+ * E2M1 value times its E8M0 scale is exactly a bf16 too, for scale bytes up
+ * to 252); the _fast entry point makes one block-scaled MFMA pass with
+ * format 4 for B.
  */
 MOE_GG_API int moe_gg_grouped_a8w4(const uint8_t *A, const uint8_t *B, uint16_t *C,
                                    const uint8_t *scale_A, const uint8_t *scale_B,

@@ -128,6 +128,62 @@ def test_wgrad_scale_only_is_exact():
     assert np.array_equal(got, ref)
 
 
+def _e4m3_times_scale(code, s):
+    e, m = (code >> 3) & 15, code & 7
+    v = (m / 8) * 2.0 ** -6 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)
+    return v * 2.0 ** (s - 127)
+
+
+def test_wgrad_extreme_scale_bytes():
+    """Element values at both ends of bf16's range.  The exact entry point converts
+    each code times its scale to bf16, which holds every such value from scale
+    bytes 3 to 246 (and larger scale bytes with codes below 2^8) exactly: here
+    2^-127 .. 2^-133 at the bottom and up to 1.875 * 2^127 at the top, against
+    products brought back to ordinary magnitudes by the other operand's scale.
+    Beyond that (2^-136, 1.75 * 2^128) the conversion rounds to bf16: to zero
+    and to infinity; the fast entry point's scaled MFMA has neither limit."""
+    torch, mg = require_gpu()
+    N, K, M = 256, 256, 128
+    off = [0, M]
+
+    def call(pairs, g_scale):
+        ca = np.full((N, M), 0x38, np.uint8)
+        sa = np.full((N, M // 32), g_scale, np.uint8)
+        cb = np.empty((K, M), np.uint8)
+        sb = np.empty((K, M // 32), np.uint8)
+        for k in range(K):
+            code, s = pairs[k % len(pairs)]
+            cb[k] = code
+            sb[k] = s
+        ref = oracle.wgrad(ca, sa, cb, sb, off)
+        got = {}
+        for fast in (False, True):
+            out = mg.wgrad_mxfp8(dev(torch, ca), dev(torch, cb), dev(torch, sa), dev(torch, sb),
+                                 dev(torch, np.asarray(off, np.int32)), fast=fast)
+            torch.cuda.synchronize()
+            got[fast] = host(out).astype(np.float64)
+        return ref, got
+
+    say("wgrad extreme scale bytes: bottom of bf16's range")
+    bottom = [(0x38, 0), (0x08, 0), (0x01, 3), (0x02, 2), (0x08, 1), (0x01, 5)]
+    ref, got = call(bottom, 227)                       # g = 2^100
+    for k, (code, s) in enumerate(bottom):
+        assert ref[0, k] == M * 2.0 ** 100 * _e4m3_times_scale(code, s)
+    assert np.array_equal(got[False], ref) and np.array_equal(got[True], ref)
+
+    say("wgrad extreme scale bytes: top of bf16's range")
+    top = [(0x77, 247), (0x70, 247), (0x38, 254), (0x7E, 246), (0x7E, 240)]
+    ref, got = call(top, 27)                           # g = 2^-100
+    assert np.array_equal(got[False], ref) and np.array_equal(got[True], ref)
+
+    say("wgrad extreme scale bytes: beyond bf16's range")
+    beyond = [(0x01, 0), (0x7E, 247)]                  # 2^-136 (with g = 2^100) and 1.75 * 2^128 (g = 2^-100)
+    ref, got = call(beyond[:1], 227)
+    assert np.array_equal(got[True], ref) and np.all(got[False] == 0.0)
+    ref, got = call(beyond[1:], 27)
+    assert np.array_equal(got[True], ref) and np.all(np.isposinf(got[False]))
+
+
 def test_wgrad_tiny_workload():
     # the tiny workload's wgrad on MX-quantised g^T and x^T (the ABI has no f32 wgrad)
     torch, mg = require_gpu()
