@@ -65,6 +65,30 @@ def test_random_dgrad_and_row_map(seed):
     assert np.array_equal(host(rows), oracle.row_experts(off, M))
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_random_dgrad_many_tiles(seed):
+    """Hundreds of 128 x 128 tiles, so the XCD-aware tile order is exercised:
+    even seeds give a tile count divisible by 8 (the reordered path), odd ones
+    not (the plain order); partial row and column tiles and unaligned bounds."""
+    torch, mg = require_gpu()
+    rng = np.random.default_rng(2500 + seed)
+    while True:
+        E = int(rng.integers(2, 12))
+        M = int(rng.integers(1500, 4200))
+        N, K = 4 * int(rng.integers(30, 200)), 4 * int(rng.integers(150, 420))
+        tiles = ((M + 127) // 128) * ((K + 127) // 128)
+        if (tiles % 8 == 0) == (seed % 2 == 0):
+            break
+    off = wl.offsets_from_counts(_counts(rng, E, M))
+    g = rng.standard_normal((M, N)).astype(np.float32)
+    W = (rng.standard_normal((E, N, K)) / np.sqrt(N)).astype(np.float32)
+    say("random dgrad, many tiles", seed, E, M, N, K, tiles, off.tolist())
+    out = mg.dgrad_f32(dev(torch, g), dev(torch, W), dev(torch, off))
+    torch.cuda.synchronize()
+    ref = oracle.dgrad(g, W, off)
+    assert oracle.dgrad_ok(host(out).astype(np.float64), ref, N)
+
+
 @pytest.mark.parametrize("seed", SEEDS)
 def test_random_grouped(seed):
     torch, mg = require_gpu()
