@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 import workloads as wl
-from gpu_helpers import dev, host, require_gpu, sample_rows, say
+from gpu_helpers import dev, host, require_gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -170,10 +170,10 @@ def test_a8w4_fast_without_outliers(name):
     assert oracle.wgrad_excess(got, ref) <= 0
 
 
-def test_a8w4_forward_full_size_sampled():
+def test_a8w4_forward_full_size():
     """The MoE forward y = x W_e^T at the 64-expert workload's full size (M=16384, K=7168 in,
-    1536 out, its offsets): sampled rows of ten experts.  W_e is one of four MXFP4-quantised
-    draws rolled along its rows per expert, so experts differ."""
+    1536 out, its offsets): every element against the oracle, the rms over the whole output.
+    W_e is one of four MXFP4-quantised draws rolled along its rows per expert, so experts differ."""
     torch, mg = require_gpu()
     w = wl.WORKLOADS[5]
     rng = np.random.default_rng(5)
@@ -195,13 +195,9 @@ def test_a8w4_forward_full_size_sampled():
                            b_fp4=True)
     torch.cuda.synchronize()
     assert tuple(got.shape) == (w.M, w.N)
-    nonempty = np.flatnonzero(np.diff(off))
-    picked = np.unique(np.concatenate([nonempty[:2], nonempty[-2:], rng.choice(nonempty, 6, replace=False)]))
-    rows = np.concatenate([int(off[e]) + sample_rows(rng, int(off[e + 1] - off[e]), 6, must=(0, 255, 256))
-                           for e in picked])
-    ref = oracle.grouped_gemm_rows(ca, sa, cb, sb, off, rows, b_format="e2m1")
-    out = host(got[rows]).astype(np.float64)
-    assert oracle.wgrad_excess(out, ref, ref_rms=np.sqrt(np.mean(ref * ref))) <= 0
+    out = host(got).astype(np.float64)
+    ref = oracle.grouped_gemm(ca, sa, cb, sb, off, b_format="e2m1")
+    assert oracle.wgrad_excess(out, ref) <= 0
 
 
 @pytest.mark.parametrize("case", ["edges", "tile", "ragged"])

@@ -205,10 +205,11 @@ def test_grouped_most_experts():
     assert oracle.wgrad_excess(got, ref) <= 0
 
 
-def test_grouped_full_size_data_gradient_sampled():
+def test_grouped_full_size_data_gradient():
     """The 64-expert data gradient at full size (M=16384, contraction 1536, 7168 outputs, the offsets
-    and g of that workload): sampled rows of ten experts against the oracle.  B[e] is one of four
-    MX-quantised W_e^T draws, rolled along its rows by a per-expert amount, so experts differ."""
+    and g of that workload): every element against the oracle, the rms over the whole output.
+    B[e] is one of four MX-quantised W_e^T draws, rolled along its rows by a per-expert amount, so
+    experts differ."""
     torch, mg = require_gpu()
     w = wl.WORKLOADS[5]
     rng = np.random.default_rng(5)
@@ -229,14 +230,7 @@ def test_grouped_full_size_data_gradient_sampled():
     got = mg.grouped_mxfp8(dev(torch, ca), dev(torch, cb), dev(torch, sa), dev(torch, sb), dev(torch, off))
     torch.cuda.synchronize()
     assert tuple(got.shape) == (w.M, w.K)
-    counts = np.diff(off)
-    nonempty = np.flatnonzero(counts)
-    picked = np.unique(np.concatenate([nonempty[:2], nonempty[-2:], rng.choice(nonempty, 6, replace=False)]))
-    rows = []
-    for e in picked:
-        o0, o1 = int(off[e]), int(off[e + 1])
-        rows.append(o0 + sample_rows(rng, o1 - o0, 6, must=(0, 255, 256, o1 - o0 - 1)))
-    rows = np.concatenate(rows)
-    ref = oracle.grouped_gemm_rows(ca, sa, cb, sb, off, rows)
-    out = host(got[rows]).astype(np.float64)
-    assert oracle.wgrad_excess(out, ref, ref_rms=np.sqrt(np.mean(ref * ref))) <= 0
+    out = host(got).astype(np.float64)
+    del got
+    ref = oracle.grouped_gemm(ca, sa, cb, sb, off)
+    assert oracle.wgrad_excess(out, ref) <= 0
