@@ -234,3 +234,33 @@ def test_grouped_full_size_data_gradient():
     del got
     ref = oracle.grouped_gemm(ca, sa, cb, sb, off)
     assert oracle.wgrad_excess(out, ref) <= 0
+
+
+def test_grouped_full_size_forward():
+    """The MoE forward y = x W_e^T with MXFP8 weights at the 64-expert workload's full size
+    (M=16384, K=7168 in, 1536 out, its offsets): every element against the oracle, the rms over
+    the whole output.  W_e is one of four MX-quantised draws rolled along its rows per expert."""
+    torch, mg = require_gpu()
+    w = wl.WORKLOADS[5]
+    rng = np.random.default_rng(5)
+    off = wl.make_offsets(5, rng)
+    x = rng.standard_normal((w.M, w.K), dtype=np.float32)
+    x[rng.random(x.shape) < 0.01] *= 64
+    ca, sa = oracle.mx_quantize(x)
+    del x
+    wrng = np.random.default_rng(57)
+    base = [oracle.mx_quantize(wrng.standard_normal((w.N, w.K), dtype=np.float32) * np.float32(0.02))
+            for _ in range(4)]
+    cb = np.empty((w.E, w.N, w.K), np.uint8)
+    sb = np.empty((w.E, w.N, w.K // 32), np.uint8)
+    for e in range(w.E):
+        q, s = base[e % 4]
+        cb[e] = np.roll(q, 29 * e, axis=0)
+        sb[e] = np.roll(s, 29 * e, axis=0)
+    say("grouped full-size forward, workload 5", w)
+    got = mg.grouped_mxfp8(dev(torch, ca), dev(torch, cb), dev(torch, sa), dev(torch, sb), dev(torch, off))
+    torch.cuda.synchronize()
+    assert tuple(got.shape) == (w.M, w.N)
+    out = host(got).astype(np.float64)
+    ref = oracle.grouped_gemm(ca, sa, cb, sb, off)
+    assert oracle.wgrad_excess(out, ref) <= 0
