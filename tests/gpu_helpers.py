@@ -31,9 +31,3 @@ def say(*args):
     print("[gpu-case]", *args, flush=True)
     sys.stdout.flush()
 
-
-def sample_rows(rng, n_rows, count, must=()):
-    picks = set(int(x) for x in must if 0 <= x < n_rows)
-    while len(picks) < min(count, n_rows):
-        picks.add(int(rng.integers(n_rows)))
-    return np.array(sorted(picks), dtype=np.int64)
