@@ -23,6 +23,11 @@
 //    along n and k) into registers, one chunk ahead (two for a pass over
 //    fewer than four row blocks), then written to a double-buffered LDS
 //    stage while the previous chunk is multiplied.
+//  * A tile wholly inside one expert, with its 128 columns inside K and N a
+//    multiple of 32 (the common case), takes dgrad_pass_full instead: chunks
+//    of 16 n whose g and W go by LDS-DMA into a ring of four LDS stages,
+//    three chunks ahead, with no bounds tests (the global latency is what
+//    one chunk ahead left exposed).
 //  * One-dimensional grid in an XCD-aware order: the tiles one XCD runs at
 //    once form a patch of row tiles x 8 column tiles sharing g rows and W
 //    columns in that XCD's L2.
@@ -180,10 +185,121 @@ __device__ __forceinline__ void dgrad_pass(const float *__restrict__ G, const fl
   }
 }
 
+// Pass over a tile whose 128 rows all belong to expert e, whose 128 columns
+// lie inside K, with N a multiple of 32 (the common case): no bounds tests and
+// a deeper pipeline than dgrad_pass.  The contraction runs in chunks of 16 n;
+// both operands of a chunk go by LDS-DMA (no staging registers) into a ring
+// of four LDS stages, chunk c + 3 issued while chunk c multiplies, so the
+// global latency has three chunks of MFMA time to hide behind (one and a half
+// of dgrad_pass's 32-n chunks, against one there).  Past the end
+// the last chunk is fetched again into the ring's next stage, which no chunk
+// reads any more, so every chunk issues the same four DMAs per wave and waits
+// on one count.
+constexpr int FC = 16;                       // n per chunk
+constexpr int FG = BM * FC * 4;              // g [128][16] f32 = 8 KB, then W [16][128] = 8 KB
+constexpr int FSTAGE = FG + FC * BK * 4;     // 16 KB
+constexpr int FNS = 4;                       // stages in the ring (64 KB)
+
+// g rows are 64 bytes, their 16-byte groups XOR-swizzled by (row/2) mod 4, so
+// the 8 rows one ds_read_b128 phase touches fall on 8 distinct bank groups;
+// W rows for n mod 16 >= 8 have column bit 5 flipped, so the two half-waves
+// of a W read land in different bank halves.
+__device__ __forceinline__ uint32_t fg_off(int row, int q /*16B group 0..3*/) {
+  return row * (FC * 4) + ((q ^ ((row >> 1) & 3)) << 4);
+}
+__device__ __forceinline__ uint32_t fw_off(int n, int col /*float index*/) {
+  return FG + n * (BK * 4) + ((col ^ (((n >> 3) & 1) << 5)) << 2);
+}
+
+__device__ __forceinline__ void dgrad_pass_full(const float *__restrict__ G, const float *__restrict__ We,
+                                                float *__restrict__ DX, uint8_t *smem, int N, int K, int r0,
+                                                int k0, int tid, int wave) {
+  const int lane = tid & 63;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int nch = N / FC;
+  const uint32_t smem_base = lds_addr(smem);
+
+  // DMA instruction j of wave w: g rows (2w + j) * 16 + lane/4, 16-byte slot
+  // lane % 4; W rows n = (2w + j) * 2 + lane/32, columns 4 (lane % 32) .. +3.
+  // Each lane fetches the global element that the swizzle puts in its slot.
+  const v4i srd_g = make_srd(G + static_cast<size_t>(r0) * N, 0xFFFFFFFFu);
+  const v4i srd_w = make_srd(We + k0, 0xFFFFFFFFu);
+  uint32_t vg[2], vw[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int row = (2 * wave + j) * 16 + (lane >> 2);
+    vg[j] = static_cast<uint32_t>(row) * N * 4u + 16u * static_cast<uint32_t>((lane & 3) ^ ((row >> 1) & 3));
+    const int n = (2 * wave + j) * 2 + (lane >> 5);
+    vw[j] = static_cast<uint32_t>(n) * K * 4u + 4u * static_cast<uint32_t>((4 * (lane & 31)) ^ (((n >> 3) & 1) << 5));
+  }
+  // chunk c's operands into stage `stage`
+  auto issue = [&](int c, int stage) __attribute__((always_inline)) {
+    const uint32_t st = __builtin_amdgcn_readfirstlane(smem_base + stage * FSTAGE + 2 * wave * 1024);
+    const uint32_t sg = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(c) * FC * 4u);
+    const uint32_t sw = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(c) * FC * K * 4u);
+    dma_b128(srd_g, vg[0], sg, st);
+    dma_b128(srd_g, vg[1], sg, st + 1024);
+    dma_b128(srd_w, vw[0], sw, st + FG);
+    dma_b128(srd_w, vw[1], sw, st + FG + 1024);
+  };
+
+  v16f acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int x = 0; x < 16; ++x) acc[i][x] = 0.f;
+
+  // lane (h, l32) takes contraction slots n = 8h + s, s = 0..7: g row 32i + l32
+  // groups 2h and 2h + 1, W rows 8h + s at column 32 wave + l32
+  const uint32_t ga_off0 = fg_off(l32, 2 * h), ga_off1 = fg_off(l32, 2 * h + 1);
+  const uint32_t w_col = 32 * wave + l32;
+
+#pragma unroll
+  for (int c = 0; c < FNS - 1; ++c) issue(min(c, nch - 1), c);
+  wait_vmcnt<8>();      // chunk 0 landed (younger: chunks 1 and 2, 4 DMAs each)
+  barrier();
+#pragma unroll 1
+  for (int c = 0; c < nch; ++c) {
+    issue(min(c + FNS - 1, nch - 1), (c + FNS - 1) % FNS);   // stage (c - 1) % 4, freed by the last barrier
+    const uint8_t *st = smem + (c % FNS) * FSTAGE;
+    v4f ga[2][4];
+    float wv[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ga[0][i] = *reinterpret_cast<const v4f *>(st + ga_off0 + i * 32 * FC * 4);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) wv[t] = *reinterpret_cast<const float *>(st + fw_off(8 * h + t, w_col));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ga[1][i] = *reinterpret_cast<const v4f *>(st + ga_off1 + i * 32 * FC * 4);
+#pragma unroll
+    for (int t = 4; t < 8; ++t) wv[t] = *reinterpret_cast<const float *>(st + fw_off(8 * h + t, w_col));
+#pragma unroll
+    for (int g2 = 0; g2 < 2; ++g2)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(ga[g2][i][t], wv[4 * g2 + t], acc[i], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);   // the chunk's MFMAs stay ahead of the wait and the barrier
+    wait_vmcnt<8>();    // chunk c + 1 landed (younger: chunks c + 2 and c + 3)
+    barrier();
+  }
+  wait_vmcnt<0>();      // the repeated DMAs past the end land before the workgroup ends
+
+  // register x of acc[i] is row i*32 + 8(x/4) + 4h + x%4 of the tile; the
+  // base is made opaque here so that the 64 store addresses are formed after
+  // the loop instead of being hoisted (and spilled) ahead of it
+  float *dst = DX + static_cast<size_t>(r0 + 4 * h) * K + k0 + wave * 32 + l32;
+  asm volatile("" : "+v"(dst));
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int x = 0; x < 16; ++x) dst[static_cast<size_t>(i * 32 + 8 * (x >> 2) + (x & 3)) * K] = acc[i][x];
+}
+
 __global__ __launch_bounds__(NTHREAD, 2) void dgrad_f32_kernel(
     const float *__restrict__ G, const float *__restrict__ W, float *__restrict__ DX,
     const int32_t *__restrict__ off, int M, int N, int K, int E) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE > FNS * FSTAGE ? 2 * STAGE : FNS * FSTAGE];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // column strip 32 wave .. +31
@@ -219,7 +335,13 @@ __global__ __launch_bounds__(NTHREAD, 2) void dgrad_f32_kernel(
       case 1: dgrad_pass<1>(G, We, DX, smem, M, N, K, r0, k0, lo, hi, ib0, tid, wave); break;
       case 2: dgrad_pass<2>(G, We, DX, smem, M, N, K, r0, k0, lo, hi, ib0, tid, wave); break;
       case 3: dgrad_pass<3>(G, We, DX, smem, M, N, K, r0, k0, lo, hi, ib0, tid, wave); break;
-      default: dgrad_pass<4>(G, We, DX, smem, M, N, K, r0, k0, lo, hi, ib0, tid, wave); break;
+      default:
+        if (lo == r0 && hi == r0 + BM && k0 + BK <= K && N >= BC && N % BC == 0 && N <= (1 << 22) &&
+            static_cast<int64_t>(N) * K < (1 << 29))
+          dgrad_pass_full(G, We, DX, smem, N, K, r0, k0, tid, wave);
+        else
+          dgrad_pass<4>(G, We, DX, smem, M, N, K, r0, k0, lo, hi, ib0, tid, wave);
+        break;
     }
   }
   // rows before off[0] or from off[E] on belong to no expert: +0.0
