@@ -18,16 +18,16 @@
 //    expert's products, and a pass over r rows costs ceil(r/32)/4 of a full
 //    one (two passes of a straddling tile together cost 1.25-1.5 passes
 //    instead of 2).
-//  * The contraction runs in chunks of 32 n.  g[128 x 32] and W_e[32 x 128]
-//    are read with 16-byte coalesced loads (g rows and W rows are contiguous
-//    along n and k) into registers, one chunk ahead (two for a pass over
-//    fewer than four row blocks), then written to a double-buffered LDS
-//    stage while the previous chunk is multiplied.
-//  * A tile wholly inside one expert, with its 128 columns inside K and N a
-//    multiple of 32 (the common case), takes dgrad_pass_full instead: chunks
-//    of 16 n whose g and W go by LDS-DMA into a ring of four LDS stages,
-//    three chunks ahead, with no bounds tests (the global latency is what
-//    one chunk ahead left exposed).
+//  * When the tile's 128 columns lie inside K and N is a nonzero multiple of
+//    32 (the common case), a pass is dgrad_pass_dma: chunks of 16 n whose g
+//    and W go by LDS-DMA into a ring of four LDS stages, three chunks ahead,
+//    with no bounds tests in the loop (the global latency is what one chunk
+//    ahead left exposed).
+//  * Otherwise dgrad_pass: the contraction in chunks of 32 n, g[128 x 32]
+//    and W_e[32 x 128] read with 16-byte coalesced loads (g rows and W rows
+//    are contiguous along n and k) into registers, one chunk ahead (two for
+//    a pass over fewer than four row blocks), then written to a
+//    double-buffered LDS stage while the previous chunk is multiplied.
 //  * One-dimensional grid in an XCD-aware order: the tiles one XCD runs at
 //    once form a patch of row tiles x 8 column tiles sharing g rows and W
 //    columns in that XCD's L2.
@@ -68,6 +68,9 @@ template <int NRB>
 __device__ __forceinline__ void dgrad_pass(const float *__restrict__ G, const float *__restrict__ We,
                                            float *__restrict__ DX, uint8_t *smem, int M, int N, int K, int r0,
                                            int k0, int lo, int hi, int ib0, int tid, int wave) {
+  // the per-lane offsets below are formed here, not hoisted to the kernel's
+  // start where they would stay live across every pass (and spill)
+  asm volatile("" : "+v"(tid));
   const int lane = tid & 63;
   const int h = lane >> 5, l32 = lane & 31;
   // global -> register loader coordinates (NRB float4 of g and 4 of W per
@@ -185,16 +188,18 @@ __device__ __forceinline__ void dgrad_pass(const float *__restrict__ G, const fl
   }
 }
 
-// Pass over a tile whose 128 rows all belong to expert e, whose 128 columns
-// lie inside K, with N a multiple of 32 (the common case): no bounds tests and
-// a deeper pipeline than dgrad_pass.  The contraction runs in chunks of 16 n;
+// The same pass, for a tile whose 128 columns lie inside K, with N a nonzero
+// multiple of 32 (the common case), with a deeper pipeline than dgrad_pass's
+// and no bounds tests in its loop.  The contraction runs in chunks of 16 n;
 // both operands of a chunk go by LDS-DMA (no staging registers) into a ring
 // of four LDS stages, chunk c + 3 issued while chunk c multiplies, so the
 // global latency has three chunks of MFMA time to hide behind (one and a half
 // of dgrad_pass's 32-n chunks, against one there).  Past the end
 // the last chunk is fetched again into the ring's next stage, which no chunk
 // reads any more, so every chunk issues the same four DMAs per wave and waits
-// on one count.
+// on one count.  All 128 g rows of the tile are fetched: rows of other
+// experts land in accumulator rows that the pass does not multiply or store,
+// rows past M fall outside the g descriptor (which reads them as zeros).
 constexpr int FC = 16;                       // n per chunk
 constexpr int FG = BM * FC * 4;              // g [128][16] f32 = 8 KB, then W [16][128] = 8 KB
 constexpr int FSTAGE = FG + FC * BK * 4;     // 16 KB
@@ -211,9 +216,15 @@ __device__ __forceinline__ uint32_t fw_off(int n, int col /*float index*/) {
   return FG + n * (BK * 4) + ((col ^ (((n >> 3) & 1) << 5)) << 2);
 }
 
-__device__ __forceinline__ void dgrad_pass_full(const float *__restrict__ G, const float *__restrict__ We,
-                                                float *__restrict__ DX, uint8_t *smem, int N, int K, int r0,
-                                                int k0, int tid, int wave) {
+template <int NRB, bool ALLROWS>
+__device__ __forceinline__ void dgrad_pass_dma(const float *__restrict__ G, const float *__restrict__ We,
+                                               float *__restrict__ DX, uint8_t *smem, int M, int N, int K, int r0,
+                                               int k0, int lo, int hi, int ib0, int tid, int wave) {
+  asm volatile("" : "+v"(tid));   // as in dgrad_pass
+  // vmcnt(0) in a form the compiler sees: a previous pass's stores and loads
+  // are complete, so the compiler places no wait of its own in the loop below
+  // (it would otherwise drain the ring's DMAs to protect their registers)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   const int lane = tid & 63;
   const int h = lane >> 5, l32 = lane & 31;
   const int nch = N / FC;
@@ -222,7 +233,7 @@ __device__ __forceinline__ void dgrad_pass_full(const float *__restrict__ G, con
   // DMA instruction j of wave w: g rows (2w + j) * 16 + lane/4, 16-byte slot
   // lane % 4; W rows n = (2w + j) * 2 + lane/32, columns 4 (lane % 32) .. +3.
   // Each lane fetches the global element that the swizzle puts in its slot.
-  const v4i srd_g = make_srd(G + static_cast<size_t>(r0) * N, 0xFFFFFFFFu);
+  const v4i srd_g = make_srd(G + static_cast<size_t>(r0) * N, static_cast<uint32_t>(min(M - r0, BM)) * N * 4u);
   const v4i srd_w = make_srd(We + k0, 0xFFFFFFFFu);
   uint32_t vg[2], vw[2];
 #pragma unroll
@@ -243,15 +254,17 @@ __device__ __forceinline__ void dgrad_pass_full(const float *__restrict__ G, con
     dma_b128(srd_w, vw[1], sw, st + FG + 1024);
   };
 
-  v16f acc[4];
+  v16f acc[NRB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NRB; ++i)
 #pragma unroll
     for (int x = 0; x < 16; ++x) acc[i][x] = 0.f;
 
-  // lane (h, l32) takes contraction slots n = 8h + s, s = 0..7: g row 32i + l32
-  // groups 2h and 2h + 1, W rows 8h + s at column 32 wave + l32
-  const uint32_t ga_off0 = fg_off(l32, 2 * h), ga_off1 = fg_off(l32, 2 * h + 1);
+  // lane (h, l32) takes contraction slots n = 8h + s, s = 0..7: g row
+  // 32(ib0 + i) + l32 groups 2h and 2h + 1, W rows 8h + s at column 32 wave + l32
+  // (the swizzle of row 32 b + l32 does not depend on b)
+  const uint32_t blk = ib0 * 32 * FC * 4;
+  const uint32_t ga_off0 = blk + fg_off(l32, 2 * h), ga_off1 = blk + fg_off(l32, 2 * h + 1);
   const uint32_t w_col = 32 * wave + l32;
 
 #pragma unroll
@@ -262,14 +275,14 @@ __device__ __forceinline__ void dgrad_pass_full(const float *__restrict__ G, con
   for (int c = 0; c < nch; ++c) {
     issue(min(c + FNS - 1, nch - 1), (c + FNS - 1) % FNS);   // stage (c - 1) % 4, freed by the last barrier
     const uint8_t *st = smem + (c % FNS) * FSTAGE;
-    v4f ga[2][4];
+    v4f ga[2][NRB];
     float wv[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ga[0][i] = *reinterpret_cast<const v4f *>(st + ga_off0 + i * 32 * FC * 4);
+    for (int i = 0; i < NRB; ++i) ga[0][i] = *reinterpret_cast<const v4f *>(st + ga_off0 + i * 32 * FC * 4);
 #pragma unroll
     for (int t = 0; t < 4; ++t) wv[t] = *reinterpret_cast<const float *>(st + fw_off(8 * h + t, w_col));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ga[1][i] = *reinterpret_cast<const v4f *>(st + ga_off1 + i * 32 * FC * 4);
+    for (int i = 0; i < NRB; ++i) ga[1][i] = *reinterpret_cast<const v4f *>(st + ga_off1 + i * 32 * FC * 4);
 #pragma unroll
     for (int t = 4; t < 8; ++t) wv[t] = *reinterpret_cast<const float *>(st + fw_off(8 * h + t, w_col));
 #pragma unroll
@@ -277,7 +290,7 @@ __device__ __forceinline__ void dgrad_pass_full(const float *__restrict__ G, con
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < NRB; ++i)
           acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(ga[g2][i][t], wv[4 * g2 + t], acc[i], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);   // the chunk's MFMAs stay ahead of the wait and the barrier
     wait_vmcnt<8>();    // chunk c + 1 landed (younger: chunks c + 2 and c + 3)
@@ -285,15 +298,20 @@ __device__ __forceinline__ void dgrad_pass_full(const float *__restrict__ G, con
   }
   wait_vmcnt<0>();      // the repeated DMAs past the end land before the workgroup ends
 
-  // register x of acc[i] is row i*32 + 8(x/4) + 4h + x%4 of the tile; the
-  // base is made opaque here so that the 64 store addresses are formed after
-  // the loop instead of being hoisted (and spilled) ahead of it
-  float *dst = DX + static_cast<size_t>(r0 + 4 * h) * K + k0 + wave * 32 + l32;
+  // register x of acc[i] is row (ib0 + i)*32 + 8(x/4) + 4h + x%4 of the tile;
+  // the pass stores the rows in [lo, hi) (ALLROWS: all 128).  The base is made opaque here so
+  // that the store addresses are formed after the loop instead of being
+  // hoisted (and spilled) ahead of it.
+  const int row0 = r0 + ib0 * 32 + 4 * h;
+  float *dst = DX + static_cast<size_t>(row0) * K + k0 + wave * 32 + l32;
   asm volatile("" : "+v"(dst));
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NRB; ++i)
 #pragma unroll
-    for (int x = 0; x < 16; ++x) dst[static_cast<size_t>(i * 32 + 8 * (x >> 2) + (x & 3)) * K] = acc[i][x];
+    for (int x = 0; x < 16; ++x) {
+      const int dr = i * 32 + 8 * (x >> 2) + (x & 3);
+      if (ALLROWS || (row0 + dr >= lo && row0 + dr < hi)) dst[static_cast<size_t>(dr) * K] = acc[i][x];
+    }
 }
 
 __global__ __launch_bounds__(NTHREAD, 2) void dgrad_f32_kernel(
@@ -323,6 +341,10 @@ __global__ __launch_bounds__(NTHREAD, 2) void dgrad_f32_kernel(
   const int e_first = __builtin_amdgcn_readfirstlane(expert_of_row(off, E, r0));
   const int e_last = __builtin_amdgcn_readfirstlane(expert_of_row(off, E, r_last));
 
+  // the LDS-DMA passes: full columns, N a nonzero multiple of 32, and offsets
+  // that fit the 32-bit buffer addressing (g: 128 rows, W_e: one expert)
+  const bool dma = k0 + BK <= K && N >= BC && N % BC == 0 && N <= (1 << 22) &&
+                   static_cast<int64_t>(N) * K < (1 << 29);
   for (int e = e_first; e <= e_last; ++e) {
     const int lo = max(clampi(off[e], 0, M), r0);
     const int hi = min(clampi(off[e + 1], 0, M), r0 + BM);
@@ -331,17 +353,25 @@ __global__ __launch_bounds__(NTHREAD, 2) void dgrad_f32_kernel(
     // the 32-row blocks [ib0, ib1) of the tile that hold this expert's rows
     const int ib0 = __builtin_amdgcn_readfirstlane((lo - r0) >> 5);
     const int ib1 = __builtin_amdgcn_readfirstlane((hi - r0 + 31) >> 5);
-    switch (ib1 - ib0) {
-      case 1: dgrad_pass<1>(G, We, DX, smem, M, N, K, r0, k0, lo, hi, ib0, tid, wave); break;
-      case 2: dgrad_pass<2>(G, We, DX, smem, M, N, K, r0, k0, lo, hi, ib0, tid, wave); break;
-      case 3: dgrad_pass<3>(G, We, DX, smem, M, N, K, r0, k0, lo, hi, ib0, tid, wave); break;
-      default:
-        if (lo == r0 && hi == r0 + BM && k0 + BK <= K && N >= BC && N % BC == 0 && N <= (1 << 22) &&
-            static_cast<int64_t>(N) * K < (1 << 29))
-          dgrad_pass_full(G, We, DX, smem, N, K, r0, k0, tid, wave);
-        else
-          dgrad_pass<4>(G, We, DX, smem, M, N, K, r0, k0, lo, hi, ib0, tid, wave);
-        break;
+    if (dma) {
+      switch (ib1 - ib0) {
+        case 1: dgrad_pass_dma<1, false>(G, We, DX, smem, M, N, K, r0, k0, lo, hi, ib0, tid, wave); break;
+        case 2: dgrad_pass_dma<2, false>(G, We, DX, smem, M, N, K, r0, k0, lo, hi, ib0, tid, wave); break;
+        case 3: dgrad_pass_dma<3, false>(G, We, DX, smem, M, N, K, r0, k0, lo, hi, ib0, tid, wave); break;
+        default:
+          if (lo == r0 && hi == r0 + BM)
+            dgrad_pass_dma<4, true>(G, We, DX, smem, M, N, K, r0, k0, lo, hi, ib0, tid, wave);
+          else
+            dgrad_pass_dma<4, false>(G, We, DX, smem, M, N, K, r0, k0, lo, hi, ib0, tid, wave);
+          break;
+      }
+    } else {
+      switch (ib1 - ib0) {
+        case 1: dgrad_pass<1>(G, We, DX, smem, M, N, K, r0, k0, lo, hi, ib0, tid, wave); break;
+        case 2: dgrad_pass<2>(G, We, DX, smem, M, N, K, r0, k0, lo, hi, ib0, tid, wave); break;
+        case 3: dgrad_pass<3>(G, We, DX, smem, M, N, K, r0, k0, lo, hi, ib0, tid, wave); break;
+        default: dgrad_pass<4>(G, We, DX, smem, M, N, K, r0, k0, lo, hi, ib0, tid, wave); break;
+      }
     }
   }
   // rows before off[0] or from off[E] on belong to no expert: +0.0
