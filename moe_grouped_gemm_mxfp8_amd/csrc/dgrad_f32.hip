@@ -13,9 +13,10 @@
 //    binary search over the offsets.  A tile inside one expert runs one pass
 //    over n with that expert's W.  A tile whose rows straddle experts runs one
 //    pass per expert present; a pass multiplies only the 32-row blocks that
-//    hold its expert's rows (the other rows' g loaded as zero) and stores only
-//    those rows at its end, so every row is written once, with exactly its own
-//    expert's products, and a pass over r rows costs ceil(r/32)/4 of a full
+//    hold its expert's rows and stores only those rows at its end, so every
+//    row is written once, with exactly its own expert's products (another
+//    expert's rows inside those blocks give accumulator rows that are never
+//    stored), and a pass over r rows costs ceil(r/32)/4 of a full
 //    one (two passes of a straddling tile together cost 1.25-1.5 passes
 //    instead of 2).
 //  * When the tile's 128 columns lie inside K and N is a nonzero multiple of
@@ -31,8 +32,8 @@
 //  * One-dimensional grid in an XCD-aware order: the tiles one XCD runs at
 //    once form a patch of row tiles x 8 column tiles sharing g rows and W
 //    columns in that XCD's L2.
-//  * Inside a chunk the MFMA k index s = 0..15 of lane group h = l/32 is
-//    n = 16h + s, so each lane reads its 16 g values with 4 ds_read_b128.  g
+//  * In dgrad_pass's chunk the MFMA k index s = 0..15 of lane group h = l/32
+//    is n = 16h + s, so each lane reads its 16 g values with 4 ds_read_b128.  g
 //    rows in LDS are 128 bytes with their 16-byte groups XOR-swizzled by
 //    (row/2) mod 8; W rows for n >= 16 have column bit 5 flipped, so the two
 //    half-waves of a W operand read land in different bank halves.
@@ -198,8 +199,9 @@ __device__ __forceinline__ void dgrad_pass(const float *__restrict__ G, const fl
 // the last chunk is fetched again into the ring's next stage, which no chunk
 // reads any more, so every chunk issues the same four DMAs per wave and waits
 // on one count.  All 128 g rows of the tile are fetched: rows of other
-// experts land in accumulator rows that the pass does not multiply or store,
-// rows past M fall outside the g descriptor (which reads them as zeros).
+// experts are either outside the pass's blocks (not multiplied) or give
+// accumulator rows that are not stored; rows past M fall outside the g
+// descriptor, which reads them as zeros without touching memory.
 constexpr int FC = 16;                       // n per chunk
 constexpr int FG = BM * FC * 4;              // g [128][16] f32 = 8 KB, then W [16][128] = 8 KB
 constexpr int FSTAGE = FG + FC * BK * 4;     // 16 KB
