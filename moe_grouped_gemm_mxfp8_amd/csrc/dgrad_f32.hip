@@ -223,9 +223,11 @@ __device__ __forceinline__ void dgrad_pass_dma(const float *__restrict__ G, cons
                                                float *__restrict__ DX, uint8_t *smem, int M, int N, int K, int r0,
                                                int k0, int lo, int hi, int ib0, int tid, int wave) {
   asm volatile("" : "+v"(tid));   // as in dgrad_pass
-  // vmcnt(0) in a form the compiler sees: a previous pass's stores and loads
-  // are complete, so the compiler places no wait of its own in the loop below
-  // (it would otherwise drain the ring's DMAs to protect their registers)
+  // vmcnt(0) in a form the compiler sees (an asm wait is opaque to it): a
+  // previous pass's stores and loads are complete, so the compiler places no
+  // wait of its own in the loop below (it would otherwise drain the ring's
+  // DMAs to protect their registers).  Immediate: vmcnt 0 (bits 3:0, 15:14),
+  // expcnt 7 (bits 6:4) and lgkmcnt 15 (bits 11:8), i.e. no wait on those.
   __builtin_amdgcn_s_waitcnt(0x0F70);
   const int lane = tid & 63;
   const int h = lane >> 5, l32 = lane & 31;
