@@ -33,6 +33,10 @@ CASES = {
     # boundaries 15, 16 and 17 rows into a 32-row block: leading and trailing 16-row half blocks,
     # passes of a half block alone, a partial column tile
     "half_blocks": (96, 160, [16, 31, 34, 31, 38, 20, 30]),
+    # the LDS-DMA pass at its edges: one row (127 of the tile's g rows past M), the fewest
+    # chunks (N = 32); several experts inside the first two 32-row blocks of a partial tile
+    "one_row": (32, 128, [1]),
+    "dma_edge_rows": (64, 256, [3, 0, 30, 2]),
 }
 
 
