@@ -410,8 +410,9 @@ def bench_quantize(torch, mg, idx, steps, warmup, cpu_baseline, rule="floor", fp
             "ms_per_step": round(ms, 4), "dtype": "f32->e2m1+e8m0" if fp4 else "f32->e4m3+e8m0",
             "config": {"workload": wl.WORKLOADS[idx].name, "R": R, "L": L},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM_GBS, 4),
-                         "traffic": read_traffic("quantize", idx) if (rule == "floor" and not fp4) else None}}
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": nbytes,
+                         "traffic": read_traffic("quantize4" if fp4 else "quantize", idx)
+                         if (fp4 or rule == "floor") else None}}
     if cpu_baseline:
         import oracle
         sub = inp["xT"][: max(1, R // 8)]

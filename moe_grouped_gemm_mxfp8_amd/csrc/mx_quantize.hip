@@ -42,8 +42,9 @@
 // 2^(floor(log2(block max)) - 2), 2 being E2M1's largest exponent as 8 is
 // E4M3's, the byte clamped to [1, 254] (1 for a zero block).  Codes: nearest
 // E2M1 value, ties to the even code, saturating at +-6, sign kept, by the
-// hardware's scaled conversion (see e2m1x8).  A lane takes 8 elements and
-// writes their codes as one dword.
+// hardware's scaled conversion (see e2m1x8).  A lane takes 4 consecutive
+// elements (loads as in mx_quantize); two neighbouring lanes join their code
+// bytes into one dword.
 #include "common.hpp"
 #include "../../include/moe_gg.h"
 
@@ -133,46 +134,49 @@ __device__ __forceinline__ uint32_t e2m1x8(const float (&a)[8], float scale) {
   return w;
 }
 
+// The MXFP4 scale byte: floor(log2 max) - 2 + 127 in [1, 254], 1 for a zero block.
+__device__ __forceinline__ uint32_t scale_byte4(uint32_t amax_bits) {
+  if (amax_bits == 0) return 1u;
+  const int s = floor_log2_bits(amax_bits) - 2 + 127;
+  return static_cast<uint32_t>(s < 1 ? 1 : (s > 254 ? 254 : s));
+}
+
 __global__ __launch_bounds__(256) void mx4_quantize_kernel(const float *__restrict__ X, uint8_t *__restrict__ Q,
                                                            uint8_t *__restrict__ S, int64_t total) {
-  // a lane takes 8 consecutive elements (two float4) and writes their codes
-  // as one dword; four lanes share a 32-element block
+  // loads as in mx_quantize_kernel (a lane takes 4 consecutive elements, a
+  // wave-wide load reads 1 KB, eight lanes share a 32-element block); lanes
+  // 2j and 2j + 1 join their two code bytes into the dword of elements
+  // 8j .. 8j + 7, which lane 2j stores
   const int lane = threadIdx.x & 63;
   const int64_t wave_global = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
   const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 6;
   for (int64_t base = wave_global * Q_WAVE_STEP; base < total; base += nwaves * Q_WAVE_STEP) {
-    v4f vv[Q_PARTS / 2][2];
+    v4f vv[Q_PARTS];
 #pragma unroll
-    for (int part = 0; part < Q_PARTS / 2; ++part) {
-      const int64_t i0 = base + part * 512 + 8 * lane;
-      const bool live = i0 < total;                       // whole 32-blocks are live or not
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        vv[part][h] = live ? __builtin_nontemporal_load(reinterpret_cast<const v4f *>(X + i0 + 4 * h))
-                           : (v4f){0.f, 0.f, 0.f, 0.f};
+    for (int part = 0; part < Q_PARTS; ++part) {
+      const int64_t i0 = base + part * 256 + 4 * lane;
+      vv[part] = i0 < total ? __builtin_nontemporal_load(reinterpret_cast<const v4f *>(X + i0)) : (v4f){0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
-    for (int part = 0; part < Q_PARTS / 2; ++part) {
-      const int64_t i0 = base + part * 512 + 8 * lane;
-      const bool live = i0 < total;
+    for (int part = 0; part < Q_PARTS; ++part) {
+      const int64_t i0 = base + part * 256 + 4 * lane;
+      const bool live = i0 < total;                       // whole 32-blocks are live or not
+      const v4f v = vv[part];
       uint32_t m = 0;
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) m = max(m, __float_as_uint(vv[part][h][i]) & 0x7FFFFFFFu);
+      for (int i = 0; i < 4; ++i) m = max(m, __float_as_uint(v[i]) & 0x7FFFFFFFu);
       m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 1)));
       m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 2)));
-      uint32_t sb = 1u;
-      if (m != 0) {
-        const int s = floor_log2_bits(m) - 2 + 127;
-        sb = static_cast<uint32_t>(s < 1 ? 1 : (s > 254 ? 254 : s));
-      }
-      const float a[8] = {vv[part][0][0], vv[part][0][1], vv[part][0][2], vv[part][0][3],
-                          vv[part][1][0], vv[part][1][1], vv[part][1][2], vv[part][1][3]};
-      const uint32_t codes = e2m1x8(a, __uint_as_float(sb << 23));   // divided by 2^(sb - 127)
+      m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 4)));
+      const uint32_t sb = scale_byte4(m);
+      const float scale = __uint_as_float(sb << 23);   // divided by 2^(sb - 127)
+      uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[0], v[1], scale, 0);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], scale, 1);
+      const uint32_t hi = static_cast<uint32_t>(__shfl_xor(static_cast<int>(w), 1));
       if (live) {
-        __builtin_nontemporal_store(codes, reinterpret_cast<uint32_t *>(Q + (i0 >> 1)));
-        if ((lane & 3) == 0) S[i0 >> 5] = static_cast<uint8_t>(sb);
+        if ((lane & 1) == 0)
+          __builtin_nontemporal_store((w & 0xFFFFu) | (hi << 16), reinterpret_cast<uint32_t *>(Q + (i0 >> 1)));
+        if ((lane & 7) == 0) S[i0 >> 5] = static_cast<uint8_t>(sb);
       }
     }
   }
@@ -181,12 +185,6 @@ __global__ __launch_bounds__(256) void mx4_quantize_kernel(const float *__restri
 constexpr int QT_TOK = 128;                // tokens per transposed tile (4 blocks of 32, one per wave)
 constexpr int QT_FEAT = 256;               // features per transposed tile (4 per lane)
 
-// The MXFP4 scale byte: floor(log2 max) - 2 + 127 in [1, 254], 1 for a zero block.
-__device__ __forceinline__ uint32_t scale_byte4(uint32_t amax_bits) {
-  if (amax_bits == 0) return 1u;
-  const int s = floor_log2_bits(amax_bits) - 2 + 127;
-  return static_cast<uint32_t>(s < 1 ? 1 : (s > 254 ? 254 : s));
-}
 
 // Wave w of a 256-thread workgroup takes the 32 tokens tok0 + 32w .. +31 of
 // the tile and lane l the features f0 + 4l .. +3: 32 float4 loads, one per
