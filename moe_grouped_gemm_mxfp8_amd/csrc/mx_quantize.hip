@@ -45,6 +45,8 @@
 // hardware's scaled conversion (see e2m1x8).  A lane takes 4 consecutive
 // elements (loads as in mx_quantize); two neighbouring lanes join their code
 // bytes into one dword.
+#include <algorithm>
+
 #include "common.hpp"
 #include "../../include/moe_gg.h"
 
@@ -300,14 +302,11 @@ int launch_quantize(bool roundup, const float *X, uint8_t *Q, uint8_t *S, int R,
   if (R == 0 || L == 0) return MOE_GG_OK;                 // nothing to quantise
   if (!X || !Q || !S || L % 32) return MOE_GG_EINVAL;
   const int64_t total = static_cast<int64_t>(R) * L;
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return MOE_GG_ELAUNCH;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    return MOE_GG_ELAUNCH;
+  // one step per wave: measured faster than a grid of 16 workgroups per CU
+  // looping over the steps (8192^2: 52.6 against 54.0 us E4M3, 46.8 against
+  // 50.9 us E2M1); the loop only serves grids beyond the launch limit
   const int64_t waves_needed = (total + Q_WAVE_STEP - 1) / Q_WAVE_STEP;
-  int64_t blocks = (waves_needed + 3) / 4;
-  const int64_t cap = static_cast<int64_t>(cus) * 16;
-  if (blocks > cap) blocks = cap;
+  const int64_t blocks = std::min<int64_t>((waves_needed + 3) / 4, 0x7FFFFFFF);
   if (roundup)
     hipLaunchKernelGGL(mx_quantize_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, X, Q, S,
                        total);
@@ -322,14 +321,11 @@ int launch_quantize4(const float *X, uint8_t *Q, uint8_t *S, int R, int L, hipSt
   if (R == 0 || L == 0) return MOE_GG_OK;                 // nothing to quantise
   if (!X || !Q || !S || L % 32) return MOE_GG_EINVAL;
   const int64_t total = static_cast<int64_t>(R) * L;
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return MOE_GG_ELAUNCH;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    return MOE_GG_ELAUNCH;
+  // one step per wave: measured faster than a grid of 16 workgroups per CU
+  // looping over the steps (8192^2: 52.6 against 54.0 us E4M3, 46.8 against
+  // 50.9 us E2M1); the loop only serves grids beyond the launch limit
   const int64_t waves_needed = (total + Q_WAVE_STEP - 1) / Q_WAVE_STEP;
-  int64_t blocks = (waves_needed + 3) / 4;
-  const int64_t cap = static_cast<int64_t>(cus) * 16;
-  if (blocks > cap) blocks = cap;
+  const int64_t blocks = std::min<int64_t>((waves_needed + 3) / 4, 0x7FFFFFFF);
   hipLaunchKernelGGL(mx4_quantize_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, X, Q, S, total);
   return hipGetLastError() == hipSuccess ? MOE_GG_OK : MOE_GG_ELAUNCH;
 }
