@@ -206,7 +206,16 @@ __global__ __launch_bounds__(256) void mx_quantize_t_kernel(const float *__restr
   __shared__ __attribute__((aligned(16))) uint8_t scales[QT_FEAT * 4];
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
-  const int bt = blockIdx.x / tiles_f, bf = blockIdx.x - bt * tiles_f;
+  // tile order: pairs of feature tiles, token tiles fastest inside a pair, so
+  // the workgroups running at once write whole rows of the output (every
+  // token tile of their features) and read 2 KB runs of the input rows
+  // (measured on 8192^2: 57.6 us, against 62.6 us with feature tiles
+  // fastest and 59.3 us with token tiles fastest over all features)
+  const int tiles_t = (R + QT_TOK - 1) / QT_TOK;
+  constexpr int FGROUP = 2;
+  const int grp = blockIdx.x / (tiles_t * FGROUP), in = blockIdx.x - grp * tiles_t * FGROUP;
+  const int gsz = min(FGROUP, tiles_f - grp * FGROUP);
+  const int bt = in / gsz, bf = grp * FGROUP + in % gsz;
   const int tok0 = bt * QT_TOK, f0 = bf * QT_FEAT;
   const int gt = tok0 + 32 * w;              // this wave's token block
   const int gf = f0 + 4 * lane;              // this lane's first feature

@@ -200,17 +200,19 @@ def test_a8w4_forward_full_size():
     assert oracle.wgrad_excess(out, ref) <= 0
 
 
-@pytest.mark.parametrize("case", ["edges", "tile", "ragged"])
+@pytest.mark.parametrize("case", ["edges", "tile", "ragged", "wide"])
 def test_mx4_quantize_transposed_bit_exact(case):
     """moe_gg_mx4_quantize_t(x) equals the oracle's MXFP4 quantisation of x^T, code for code."""
     torch, mg = require_gpu()
-    rng = np.random.default_rng({"edges": 21, "tile": 22, "ragged": 23}[case])
+    rng = np.random.default_rng({"edges": 21, "tile": 22, "ragged": 23, "wide": 24}[case])
     if case == "edges":
         x = np.ascontiguousarray(np.concatenate([_mx4_edges(), np.zeros((2, 128), np.float32)]).T)   # [128, 12]
     elif case == "tile":
         x = rng.standard_normal((256, 512)).astype(np.float32)
-    else:                                                     # partial tiles in both directions
+    elif case == "ragged":                                    # partial tiles in both directions
         x = (rng.standard_normal((160, 300)) * np.exp2(rng.integers(-40, 40, (1, 300)))).astype(np.float32)
+    else:                                                     # 3 x 3 tiles, both partial
+        x = (rng.standard_normal((288, 600)) * np.exp2(rng.integers(-30, 30, (1, 600)))).astype(np.float32)
     say("mx4_quantize_t", case, x.shape)
     q, s = mg.mx4_quantize_t(dev(torch, x))
     torch.cuda.synchronize()

@@ -66,20 +66,22 @@ def test_quantize_workload_inputs(idx):
         assert np.array_equal(host(q), want_q)
 
 
-@pytest.mark.parametrize("case", ["edge", "tile", "ragged", "tall"])
+@pytest.mark.parametrize("case", ["edge", "tile", "ragged", "tall", "wide"])
 def test_quantize_transposed_bit_exact(case):
     """moe_gg_mx_quantize_t(x) equals the oracle's quantisation of x^T, code for code."""
     torch, mg = require_gpu()
-    rng = np.random.default_rng({"edge": 11, "tile": 12, "ragged": 13, "tall": 14}[case])
+    rng = np.random.default_rng({"edge": 11, "tile": 12, "ragged": 13, "tall": 14, "wide": 15}[case])
     if case == "edge":
         x = np.ascontiguousarray(_edge_input().T)            # [128 tokens, 12 features]
     elif case == "tile":
         x = rng.standard_normal((256, 128)).astype(np.float32)
     elif case == "ragged":                                    # partial tiles in both directions
         x = (rng.standard_normal((160, 100)) * np.exp2(rng.integers(-40, 40, (1, 100)))).astype(np.float32)
-    else:
+    elif case == "tall":
         x = rng.standard_normal((4096 + 32, 36)).astype(np.float32)
         x[rng.random(x.shape) < 0.01] *= 64
+    else:   # 3 x 3 tiles, both partial: a pair of feature tiles, then a single one in the tile order
+        x = (rng.standard_normal((288, 600)) * np.exp2(rng.integers(-30, 30, (1, 600)))).astype(np.float32)
     say("quantize_t", case, x.shape)
     q, s = mg.mx_quantize_t(dev(torch, x))
     torch.cuda.synchronize()
