@@ -24,18 +24,20 @@
 //
 // mx_quantize: HBM-bound streaming kernel; rows never split a block (L % 32
 // == 0), so the [R][L] input is a flat sequence of blocks.  A wave handles 1024
-// elements per step as four coalesced 1 KB float4 sweeps, all loads issued
-// before any block is converted; the 8 lanes that
-// share a block reduce its max with xor shuffles; each lane writes its 4 codes
-// as one dword and the first lane of each block the scale byte.
+// elements as four coalesced 1 KB float4 sweeps, all loads issued before any
+// block is converted, and the grid gives every wave one such step; the 8
+// lanes that share a block reduce its max with xor shuffles; each lane writes
+// its 4 codes as one dword and the first lane of each block the scale byte.
 //
 // mx_quantize_t: the same codes for the transpose, so that g [M][N] (tokens x
 // features) becomes g^T codes [N][M] with one scale per 32 tokens without a
-// separate transpose pass.  A 256-thread workgroup takes 128 tokens x 64
-// features: coalesced float4 loads of the token rows into an LDS tile held
-// feature-major, then one thread per (feature, 32-token block) computes the
-// block's scale and writes its 32 codes as two 16-byte stores, four threads
-// covering a feature row's 128 bytes.
+// separate transpose pass.  A 256-thread workgroup takes 128 tokens x 256
+// features: wave w the 32-token block w, lane l the features 4l..4l+3, held
+// in registers after 32 float4 loads (each wave-wide load reads 1 KB of a
+// token row); maxima, scales and codes come out of registers, and only the
+// code and scale bytes pass through LDS, so that each feature row of the
+// tile leaves as one 128-byte line.  Workgroups take the tiles in pairs of
+// feature tiles, token tiles fastest inside a pair.
 //
 // mx4_quantize: MXFP4 (E2M1 codes, two per byte, element 2i in the low
 // nibble; the operand order of the gfx950 MFMA's format 4).  Scale
