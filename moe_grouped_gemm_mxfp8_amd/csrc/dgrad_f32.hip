@@ -207,12 +207,13 @@ constexpr int FG = BM * FC * 4;              // g [128][16] f32 = 8 KB, then W [
 constexpr int FSTAGE = FG + FC * BK * 4;     // 16 KB
 constexpr int FNS = 4;                       // stages in the ring (64 KB)
 
-// g rows are 64 bytes, their 16-byte groups XOR-swizzled by (row/2) mod 4, so
-// the 8 rows one ds_read_b128 phase touches fall on 8 distinct bank groups;
+// g rows are 64 bytes, their 16-byte groups XOR-swizzled by (row/4) mod 4, so
+// the 16 rows one ds_read_b128 phase touches (16 lanes, 64 banks of 4 bytes)
+// fall on 16 distinct 16-byte bank groups;
 // W rows for n mod 16 >= 8 have column bit 5 flipped, so the two half-waves
 // of a W read land in different bank halves.
 __device__ __forceinline__ uint32_t fg_off(int row, int q /*16B group 0..3*/) {
-  return row * (FC * 4) + ((q ^ ((row >> 1) & 3)) << 4);
+  return row * (FC * 4) + ((q ^ ((row >> 2) & 3)) << 4);
 }
 __device__ __forceinline__ uint32_t fw_off(int n, int col /*float index*/) {
   return FG + n * (BK * 4) + ((col ^ (((n >> 3) & 1) << 5)) << 2);
@@ -243,7 +244,7 @@ __device__ __forceinline__ void dgrad_pass_dma(const float *__restrict__ G, cons
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int row = (2 * wave + j) * 16 + (lane >> 2);
-    vg[j] = static_cast<uint32_t>(row) * N * 4u + 16u * static_cast<uint32_t>((lane & 3) ^ ((row >> 1) & 3));
+    vg[j] = static_cast<uint32_t>(row) * N * 4u + 16u * static_cast<uint32_t>((lane & 3) ^ ((row >> 2) & 3));
     const int n = (2 * wave + j) * 2 + (lane >> 5);
     vw[j] = static_cast<uint32_t>(n) * K * 4u + 4u * static_cast<uint32_t>((4 * (lane & 31)) ^ (((n >> 3) & 1) << 5));
   }
